@@ -25,8 +25,9 @@
  * With these rules the outcome is unique.
  *
  * Invalid ids never trap: -1 is padding (output -1, no effect), an id outside
- * [0, host_rows) or outside the tail window sets ORACLE_BAD_ID, a repeat of an
- * earlier id in the same step sets ORACLE_DUP_ID; both give output -1.
+ * [0, host_rows) or at/after tail0 but outside the tail window sets
+ * ORACLE_BAD_ID, a repeat of an earlier valid id in the same step sets
+ * ORACLE_DUP_ID; both give output -1.
  */
 #include <stdint.h>
 #include <stdlib.h>
@@ -91,13 +92,12 @@ int oracle_resolve(const oracle_dims* d, int32_t* slot_tok, int32_t* stamp, int3
     out[i] = -1;
     if (x == -1) continue;
     if (x < 0 || x >= H) { status |= ORACLE_BAD_ID; continue; }
+    const int resident = has_tail && (int64_t)x >= (int64_t)tail0;
+    if (resident && (int64_t)x - (int64_t)tail0 >= (int64_t)T) { status |= ORACLE_BAD_ID; continue; }
+    /* repeats are looked for among valid ids only */
     if (seen[x]) { status |= ORACLE_DUP_ID; continue; }
     seen[x] = 1;
-    if (has_tail && (int64_t)x >= (int64_t)tail0) {
-      if ((int64_t)x - (int64_t)tail0 < (int64_t)T) out[i] = B + (x - tail0);
-      else status |= ORACLE_BAD_ID;
-      continue;
-    }
+    if (resident) { out[i] = B + (x - tail0); continue; }
     if (page[x] != -1) {
       out[i] = page[x];
       hit[page[x]] = 1;

@@ -42,15 +42,16 @@ class ListLRU:
             if not (0 <= x < self.H):
                 status |= BAD_ID
                 continue
+            in_tail = tail0 is not None and x >= tail0
+            if in_tail and x - tail0 >= self.T:
+                status |= BAD_ID
+                continue
             if x in seen:
                 status |= DUP_ID
                 continue
             seen.add(x)
-            if tail0 is not None and x >= tail0:
-                if x - tail0 < self.T:
-                    out[i] = self.B + (x - tail0)
-                else:
-                    status |= BAD_ID
+            if in_tail:
+                out[i] = self.B + (x - tail0)
                 continue
             if x in self.where:
                 out[i] = self.where[x]

@@ -291,6 +291,7 @@ MUTANTS = {
     "wrong host row": ("host + (int64_t)x * rb", "host + (int64_t)(x ^ 1) * rb"),
     "victims from the newest end": ("const int32_t v = cand[j].val;", "const int32_t v = cand[c - 1 - j].val;"),
     "duplicate not rejected": ("if (seen[x]) { status |= ORACLE_DUP_ID; continue; }", ""),
+    "tail window not checked": ("if (resident && (int64_t)x - (int64_t)tail0 >= (int64_t)T)", "if (0)"),
     "tail index off by one": ("out[i] = B + (x - tail0);", "out[i] = B + (x - tail0) + 1;"),
     "step counter not advanced": ("*t_io = t + 1;", "*t_io = t;"),
 }
