@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the HiSparse swap-in path on one MI355X.
+
+A step is one hs_resolve over every request of the workload (one decode step): hit test, LRU victims, page
+table update and the copy of every missed row from pinned host memory into HBM. Inputs (the per-step top-k
+ids) are staged in HBM before the timed region. The JSON line reports resolved top-k entries/s (the value),
+the miss-copy rate against the host link, HBM figures, the roofline of the resolve kernel and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PCIE5_X16_GBPS = 64.0      # MI355X host link, PCIe 5.0 x16, per direction (published)
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E (published)
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=960)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="concurrency_256req_L32768_B4096_k2048")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true")
+    return ap.parse_args()
+
+
+def link_and_hbm_probes(torch):
+    """Measured H2D link peak (pinned 1 GiB, hipMemcpyAsync via torch, median of 10) and HBM copy rate."""
+    n = 1 << 30
+    h = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+    d = torch.empty(n, dtype=torch.uint8, device="cuda")
+    d2 = torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def med(fn, reps=10):
+        ts = []
+        fn()
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    link_ms = med(lambda: d.copy_(h, non_blocking=True))
+    hbm_ms = med(lambda: d2.copy_(d))
+    del h, d, d2
+    torch.cuda.empty_cache()
+    return n / link_ms / 1e6, 2 * n / hbm_ms / 1e6
+
+
+def cpu_baseline(w, ids, seconds: float):
+    """The oracle, as it is, on the first requests of the same streams (its own rows from the generator)."""
+    import numpy as np
+    import oracle
+    import workload
+    n_steps = ids.shape[1]
+    # size the sample from a short calibration on one request
+    cal = oracle.Oracle(1, w.buffer_slots, w.top_k, w.host_rows, w.row_bytes,
+                        host=np.zeros((1, w.host_rows, w.row_bytes), np.uint8))
+    t0 = time.perf_counter()
+    cal_steps = min(n_steps, 64)
+    for t in range(cal_steps):
+        cal.step(ids[:1, t])
+    per_req_step = (time.perf_counter() - t0) / cal_steps
+    n_req = max(1, min(w.num_requests, int(seconds / (per_req_step * n_steps))))
+    host = np.empty((n_req, w.host_rows, w.row_bytes), np.uint8)
+    for j in range(n_req):
+        workload.fill_rows(host[j].view(np.uint16).reshape(w.host_rows, w.row_elems), j * w.host_rows, w.host_rows,
+                           w.row_elems, w.row_seed)
+    tail = tail0 = None
+    if w.tail_tokens:
+        tail = np.ascontiguousarray(host[:, w.tail0:w.tail0 + w.tail_tokens])
+        tail0 = np.full(n_req, w.tail0, np.int32)
+    o = oracle.Oracle(n_req, w.buffer_slots, w.top_k, w.host_rows, w.row_bytes, T=w.tail_tokens, host=host, tail=tail)
+    sub = np.ascontiguousarray(ids[:n_req])
+    misses = 0
+    t0 = time.perf_counter()
+    for t in range(n_steps):
+        _, miss, _, _ = o.step(sub[:, t], tail0, gather=w.fused_gather)
+        misses += int(miss.sum())
+    dt = time.perf_counter() - t0
+    entries = n_req * n_steps * w.top_k
+    return {"value": entries / dt, "unit": "entries/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_req} of {w.num_requests} requests x all {n_steps} steps ({dt:.1f} s, single thread)",
+            "miss_copy_GBps": misses * w.row_bytes / dt / 1e9}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the swap-in path shards by request with no exchange between GPUs, "
+              f"so --gpus {args.gpus} is not run here", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import hierarchical_memory_amd as hm
+    import workload
+
+    by_name = {w.name: w for w in workload.ALL}
+    w = by_name[args.workload]
+    K, W = args.steps, args.warmup
+    n_steps = W + K
+    R, k, B, H, T, rb = w.num_requests, w.top_k, w.buffer_slots, w.host_rows, w.tail_tokens, w.row_bytes
+    if w.grow and w.L0 + n_steps > H:
+        raise SystemExit(f"{n_steps} steps outgrow the {H}-row host pool of {w.name}")
+    torch.cuda.set_device(0)
+
+    link_peak = hbm_copy = None
+    if not args.no_probes:
+        link_peak, hbm_copy = link_and_hbm_probes(torch)
+        log(f"[bench] measured H2D link {link_peak:.1f} GB/s, HBM copy {hbm_copy:.0f} GB/s (read+write)")
+
+    log(f"[bench] {w.name}: R={R} k={k} B={B} host_rows={H} T={T}, warmup {W} + timed {K} steps")
+    t0 = time.perf_counter()
+    sw = hm.SwapIn(hm.config(R, k, B, 0.0, rb, H, T))
+    workload.fill_rows_ptr(sw.host_pool_address(), 0, R * H, w.row_elems, w.row_seed)
+    tail0 = None
+    if T:
+        pool = sw.host_pool()
+        sw.tail.copy_(torch.from_numpy(np.ascontiguousarray(pool[:, w.tail0:w.tail0 + T])))
+        tail0 = torch.full((R,), w.tail0, dtype=torch.int32, device="cuda")
+    ids = workload.streams(w, n_steps=n_steps)                      # [R, steps, k]
+    topk = torch.from_numpy(np.ascontiguousarray(ids.transpose(1, 0, 2))).cuda()  # [steps, R, k] in HBM
+    out = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    miss = torch.zeros((n_steps, R), dtype=torch.int32, device="cuda")
+    status = torch.zeros((n_steps, R), dtype=torch.int32, device="cuda")
+    g = torch.empty((R, k, rb), dtype=torch.uint8, device="cuda") if w.fused_gather else None
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.perf_counter() - t0:.1f} s (pool {R * H * rb / 1e9:.2f} GB pinned)")
+
+    stream = torch.cuda.current_stream()
+    for t in range(W):
+        hm.hs_resolve(sw.ctx, topk[t], tail0, out, miss[t], status[t], g, stream)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    torch.cuda.synchronize()   # one process, one GPU: the barrier is this synchronize
+    wall0 = time.perf_counter()
+    for i in range(K):
+        evs[i].record(stream)
+        hm.hs_resolve(sw.ctx, topk[W + i], tail0, out, miss[W + i], status[W + i], g, stream)
+    evs[K].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed_ms = evs[0].elapsed_time(evs[K])
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(K)])
+    st = status[W:].cpu().numpy()
+    if st.any():
+        raise SystemExit(f"device status bits set during the timed steps: {np.unique(st)}")
+    m = miss[W:].cpu().numpy().astype(np.int64)
+    total_miss = int(m.sum())
+    secs = elapsed_ms / 1e3
+    entries = K * R * k
+    value = entries / secs
+    miss_bytes = total_miss * rb
+    miss_gbps = miss_bytes / secs / 1e9
+    launch_ms = elapsed_ms / K
+    # algorithmic HBM bytes of one resolve: per request 4k ids read + 4B slot table read + 4B LRU state read and
+    # write (2B order list each way) + 4k outputs + stamps of hits and misses + 12 per miss (slot table, page
+    # entry, evicted page entry) + the fetched rows written; fused gather adds k rows written and hit/tail rows read
+    meta = R * (12 * k + 8 * B) + 12 * total_miss / K
+    hbm_bytes = meta + miss_bytes / K
+    if w.fused_gather:
+        hbm_bytes += R * k * rb + (R * k - total_miss / K) * rb
+    hbm_gbps = hbm_bytes / (launch_ms / 1e3) / 1e9
+    log(f"[bench] {K} steps in {elapsed_ms:.1f} ms ({launch_ms:.3f} ms/step, wall {wall:.2f} s): "
+        f"{value / 1e6:.1f} M entries/s, misses/request-step {total_miss / (K * R):.1f}, miss copy {miss_gbps:.1f} GB/s")
+    rep = {
+        "metric": "resolved top-k entries/s (+ miss-copy GB/s vs host link, HBM), 1 GPU",
+        "value": value,
+        "unit": "entries/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": launch_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "requests": R, "top_k": k, "buffer_slots": B, "host_rows": H,
+                   "tail_tokens": T, "row_bytes": rb, "fused_gather": w.fused_gather,
+                   "timed_steps": [W, W + K]},
+        "miss_copy_GBps": miss_gbps,
+        "miss_rows_per_request_step": total_miss / (K * R),
+        "measured_link_peak_GBps": link_peak,
+        "miss_copy_frac_of_measured_link": (miss_gbps / link_peak) if link_peak else None,
+        "measured_hbm_copy_GBps": hbm_copy,
+        "step_ms_p10_p50_p90": [float(np.percentile(per, q)) for q in (10, 50, 90)],
+        "roofline": {"bound": "host_link", "achieved": miss_gbps, "peak": PCIE5_X16_GBPS, "unit": "GB/s",
+                     "frac": miss_gbps / PCIE5_X16_GBPS, "traffic": None,
+                     "kernel": "resolve_kernel",
+                     "algorithmic_bytes_per_launch": miss_bytes / K},
+        "hbm": {"achieved": hbm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hbm_gbps / HBM_PEAK_GBPS,
+                "algorithmic_bytes_per_launch": hbm_bytes},
+    }
+    sw.close()
+    del topk
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline ...")
+        rep["cpu_baseline"] = cpu_baseline(w, ids, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {rep['cpu_baseline']['value'] / 1e6:.2f} M entries/s ({rep['cpu_baseline']['sample']})")
+    print(json.dumps(rep), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

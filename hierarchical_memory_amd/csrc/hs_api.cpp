@@ -1,0 +1,297 @@
+// C ABI of the HiSparse swap-in path: argument checks, the pinned host pool, launches.
+#include "hisparse.h"
+#include "hs_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+struct hs_ctx {
+  hs_config cfg;
+  int32_t H;             // host rows per request
+  hs::Layout layout;
+  int device;
+  void* pool_host;       // pinned, mapped host pool
+  void* pool_dev;        // its device address
+  uint64_t pool_bytes;
+  bool bound;
+  hs_device_views views;
+};
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return HS_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(HS_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Validates cfg and derives the host rows and LDS layout. Host-only.
+int check_config(const hs_config* cfg, int32_t* H_out, hs::Layout* L_out) {
+  if (!cfg) return fail(HS_E_INVALID, "config is NULL");
+  if (cfg->num_requests < 1) return fail(HS_E_INVALID, "num_requests must be >= 1 (got %d)", cfg->num_requests);
+  if (cfg->top_k < 1 || cfg->top_k > hs::kMaxTopK)
+    return fail(HS_E_INVALID, "top_k must be in [1, %d] (got %d)", hs::kMaxTopK, cfg->top_k);
+  if (cfg->device_buffer_size < cfg->top_k || cfg->device_buffer_size > hs::kMaxSlots)
+    return fail(HS_E_INVALID, "device_buffer_size must be in [top_k, %d] (got %d, top_k %d)", hs::kMaxSlots,
+                cfg->device_buffer_size, cfg->top_k);
+  if (cfg->row_bytes < 16 || cfg->row_bytes % 16 != 0 || cfg->row_bytes > (1 << 20))
+    return fail(HS_E_INVALID, "row_bytes must be a multiple of 16 in [16, 1 MiB] (got %d)", cfg->row_bytes);
+  if (cfg->tail_tokens < 0) return fail(HS_E_INVALID, "tail_tokens must be >= 0 (got %d)", cfg->tail_tokens);
+  if (cfg->max_context < 0) return fail(HS_E_INVALID, "max_context must be >= 0 (got %d)", cfg->max_context);
+  int64_t H = cfg->max_context;
+  if (H == 0) {
+    const double want = std::ceil((double)cfg->host_to_device_ratio * (double)cfg->device_buffer_size);
+    if (!(cfg->host_to_device_ratio > 0.0f) || !std::isfinite(want) || want > 2147483647.0)
+      return fail(HS_E_INVALID, "host_to_device_ratio must be > 0 and give at most 2^31-1 rows (got %g)",
+                  (double)cfg->host_to_device_ratio);
+    H = (int64_t)want;
+  }
+  if (H < 1) return fail(HS_E_INVALID, "host rows per request must be >= 1");
+  const hs::Layout L = hs::make_layout(cfg->top_k, cfg->device_buffer_size, (int)H);
+  // 1 KiB of the 160 KiB of a gfx950 compute unit stays for the kernel's static LDS
+  if (L.total > 159u * 1024u)
+    return fail(HS_E_INVALID,
+                "this shape needs %u bytes of LDS per workgroup (top_k %d, buffer %d, host rows %lld), "
+                "more than the 159 KiB one resolve workgroup may use on gfx950",
+                L.total, cfg->top_k, cfg->device_buffer_size, (long long)H);
+  *H_out = (int32_t)H;
+  *L_out = L;
+  return HS_OK;
+}
+
+void fill_sizes(const hs_config* cfg, int32_t H, const hs::Layout& L, hs_sizes* s) {
+  const uint64_t R = (uint64_t)cfg->num_requests, k = (uint64_t)cfg->top_k, B = (uint64_t)cfg->device_buffer_size;
+  const uint64_t rb = (uint64_t)cfg->row_bytes, T = (uint64_t)cfg->tail_tokens;
+  s->host_rows = H;
+  s->host_pool_bytes = R * (uint64_t)H * rb;
+  s->hot_bytes = R * B * rb;
+  s->tail_bytes = R * T * rb;
+  s->slot_tok_bytes = R * B * 4;
+  s->stamp_bytes = R * B * 4;
+  s->lru_order_bytes = R * B * 2;
+  s->page_bytes = R * (uint64_t)H * 4;
+  s->step_bytes = R * 4;
+  s->topk_bytes = R * k * 4;
+  s->out_bytes = R * k * 4;
+  s->gather_bytes = R * k * rb;
+  s->lds_bytes = L.total;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_ready(hs_ctx* ctx) {
+  if (!ctx) return fail(HS_E_INVALID, "context is NULL");
+  if (!ctx->bound) return fail(HS_E_STATE, "device buffers not bound (call hs_bind_device first)");
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hs_required_sizes(const hs_config* cfg, hs_sizes* out) {
+  if (!out) return fail(HS_E_INVALID, "sizes output is NULL");
+  int32_t H;
+  hs::Layout L;
+  int rc = check_config(cfg, &H, &L);
+  if (rc) return rc;
+  fill_sizes(cfg, H, L, out);
+  return ok();
+}
+
+int hs_create(const hs_config* cfg, hs_ctx** out) {
+  if (!out) return fail(HS_E_INVALID, "context output is NULL");
+  *out = nullptr;
+  int32_t H;
+  hs::Layout L;
+  int rc = check_config(cfg, &H, &L);
+  if (rc) return rc;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int lds_max = 0;
+  e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(max shared memory per block)");
+  if ((int64_t)L.total + 1024 > (int64_t)lds_max)
+    return fail(HS_E_INVALID, "this shape needs %u bytes of LDS per workgroup, the device allows %d", L.total,
+                lds_max);
+  e = hs::set_resolve_lds_limit(L.total);
+  if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(resolve kernel LDS)");
+
+  hs_ctx* ctx = new (std::nothrow) hs_ctx();
+  if (!ctx) return fail(HS_E_NOMEM, "out of host memory for the context");
+  ctx->cfg = *cfg;
+  ctx->H = H;
+  ctx->layout = L;
+  ctx->device = dev;
+  ctx->pool_bytes = (uint64_t)cfg->num_requests * (uint64_t)H * (uint64_t)cfg->row_bytes;
+  // Pinned host memory mapped into the GPU's address space; the resolve kernel reads missed rows
+  // from it directly over the host link. Coherent: host writes made after a kernel has read the
+  // pool are seen by later kernels.
+  e = hipHostMalloc(&ctx->pool_host, ctx->pool_bytes, hipHostMallocMapped | hipHostMallocCoherent);
+  if (e != hipSuccess || !ctx->pool_host) {
+    (void)hipGetLastError();
+    delete ctx;
+    return fail(HS_E_NOMEM, "hipHostMalloc of a %llu-byte pinned host pool failed: %s",
+                (unsigned long long)(cfg->num_requests * (uint64_t)H * (uint64_t)cfg->row_bytes),
+                hipGetErrorString(e));
+  }
+  e = hipHostGetDevicePointer(&ctx->pool_dev, ctx->pool_host, 0);
+  if (e != hipSuccess) {
+    (void)hipHostFree(ctx->pool_host);
+    delete ctx;
+    return hip_fail(e, "hipHostGetDevicePointer");
+  }
+  *out = ctx;
+  return ok();
+}
+
+int hs_host_pool(hs_ctx* ctx, void** host_base, uint64_t* request_stride_bytes, int32_t* host_rows) {
+  if (!ctx) return fail(HS_E_INVALID, "context is NULL");
+  if (host_base) *host_base = ctx->pool_host;
+  if (request_stride_bytes) *request_stride_bytes = (uint64_t)ctx->H * (uint64_t)ctx->cfg.row_bytes;
+  if (host_rows) *host_rows = ctx->H;
+  return ok();
+}
+
+int hs_bind_device(hs_ctx* ctx, const hs_device_views* v) {
+  if (!ctx) return fail(HS_E_INVALID, "context is NULL");
+  if (!v) return fail(HS_E_INVALID, "views are NULL");
+  hs_sizes s;
+  fill_sizes(&ctx->cfg, ctx->H, ctx->layout, &s);
+  struct Need { const void* p; uint64_t have, need; const char* name; uintptr_t align; };
+  const Need needs[] = {
+      {v->hot, v->hot_bytes, s.hot_bytes, "hot", 16},
+      {v->slot_tok, v->slot_tok_bytes, s.slot_tok_bytes, "slot_tok", 4},
+      {v->stamp, v->stamp_bytes, s.stamp_bytes, "stamp", 4},
+      {v->lru_order, v->lru_order_bytes, s.lru_order_bytes, "lru_order", 2},
+      {v->page, v->page_bytes, s.page_bytes, "page", 4},
+      {v->step, v->step_bytes, s.step_bytes, "step", 4},
+  };
+  for (const Need& n : needs) {
+    if (!n.p) return fail(HS_E_INVALID, "device buffer '%s' is NULL", n.name);
+    if (n.have < n.need)
+      return fail(HS_E_INVALID, "device buffer '%s' has %llu bytes, needs %llu", n.name, (unsigned long long)n.have,
+                  (unsigned long long)n.need);
+    if (!aligned(n.p, n.align)) return fail(HS_E_INVALID, "device buffer '%s' is not %d-byte aligned", n.name,
+                                             (int)n.align);
+  }
+  if (ctx->cfg.tail_tokens > 0) {
+    if (!v->tail) return fail(HS_E_INVALID, "device buffer 'tail' is NULL but tail_tokens = %d", ctx->cfg.tail_tokens);
+    if (v->tail_bytes < s.tail_bytes)
+      return fail(HS_E_INVALID, "device buffer 'tail' has %llu bytes, needs %llu", (unsigned long long)v->tail_bytes,
+                  (unsigned long long)s.tail_bytes);
+    if (!aligned(v->tail, 16)) return fail(HS_E_INVALID, "device buffer 'tail' is not 16-byte aligned");
+  }
+  ctx->views = *v;
+  ctx->bound = true;
+  return ok();
+}
+
+int hs_reset(hs_ctx* ctx, const int32_t* d_request_ids, int32_t n, void* stream) {
+  int rc = check_ready(ctx);
+  if (rc) return rc;
+  int blocks;
+  if (d_request_ids) {
+    if (n < 0) return fail(HS_E_INVALID, "n must be >= 0 when request ids are given (got %d)", n);
+    blocks = n;
+  } else {
+    if (n >= 0) return fail(HS_E_INVALID, "request ids are NULL: pass n < 0 to reset every request");
+    blocks = ctx->cfg.num_requests;
+  }
+  hs::ResetArgs a{};
+  a.R = ctx->cfg.num_requests;
+  a.B = ctx->cfg.device_buffer_size;
+  a.H = ctx->H;
+  a.ids = d_request_ids;
+  a.slot_tok = ctx->views.slot_tok;
+  a.stamp = ctx->views.stamp;
+  a.order = ctx->views.lru_order;
+  a.page = ctx->views.page;
+  a.step = ctx->views.step;
+  hipError_t e = hs::launch_reset(a, blocks, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "reset launch");
+  return ok();
+}
+
+int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
+               int32_t* d_status, void* d_gather, void* stream) {
+  int rc = check_ready(ctx);
+  if (rc) return rc;
+  if (!d_topk || !d_out || !d_miss || !d_status)
+    return fail(HS_E_INVALID, "topk, out, miss and status must not be NULL");
+  if (d_gather && !aligned(d_gather, 16)) return fail(HS_E_INVALID, "gather output is not 16-byte aligned");
+  if (ctx->cfg.tail_tokens == 0 && d_tail0)
+    return fail(HS_E_INVALID, "tail0 given but the context has no tail (tail_tokens = 0)");
+  hs::ResolveArgs a{};
+  a.R = ctx->cfg.num_requests;
+  a.k = ctx->cfg.top_k;
+  a.B = ctx->cfg.device_buffer_size;
+  a.H = ctx->H;
+  a.T = ctx->cfg.tail_tokens;
+  a.row16 = ctx->cfg.row_bytes / 16;
+  a.L = ctx->layout;
+  a.host = (const hs::v4u*)ctx->pool_dev;
+  a.hot = (hs::v4u*)ctx->views.hot;
+  a.tail = (const hs::v4u*)ctx->views.tail;
+  a.slot_tok = ctx->views.slot_tok;
+  a.stamp = ctx->views.stamp;
+  a.order = ctx->views.lru_order;
+  a.page = ctx->views.page;
+  a.step = ctx->views.step;
+  a.topk = d_topk;
+  a.tail0 = d_tail0;
+  a.out = d_out;
+  a.miss = d_miss;
+  a.status = d_status;
+  a.gather = (hs::v4u*)d_gather;
+  hipError_t e = hs::launch_resolve(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "resolve launch");
+  return ok();
+}
+
+int hs_gather(hs_ctx* ctx, const int32_t* d_out, void* d_gather, void* stream) {
+  int rc = check_ready(ctx);
+  if (rc) return rc;
+  if (!d_out || !d_gather) return fail(HS_E_INVALID, "out and gather must not be NULL");
+  if (!aligned(d_gather, 16)) return fail(HS_E_INVALID, "gather output is not 16-byte aligned");
+  hs::GatherArgs a{};
+  a.R = ctx->cfg.num_requests;
+  a.k = ctx->cfg.top_k;
+  a.B = ctx->cfg.device_buffer_size;
+  a.T = ctx->cfg.tail_tokens;
+  a.row16 = ctx->cfg.row_bytes / 16;
+  a.out = d_out;
+  a.hot = (const hs::v4u*)ctx->views.hot;
+  a.tail = (const hs::v4u*)ctx->views.tail;
+  a.gather = (hs::v4u*)d_gather;
+  hipError_t e = hs::launch_gather(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+void hs_destroy(hs_ctx* ctx) {
+  if (!ctx) return;
+  if (ctx->pool_host) (void)hipHostFree(ctx->pool_host);
+  delete ctx;
+}
+
+const char* hs_last_error(void) { return g_err; }
+
+}  // extern "C"

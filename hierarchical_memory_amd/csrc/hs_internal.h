@@ -1,0 +1,101 @@
+// Internal declarations shared by the C ABI (hs_api.cpp) and the kernels (hs_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hs {
+
+constexpr int kThreads = 1024;            // resolve workgroup: 16 wave64s
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxTopK = 8192;
+constexpr int kMaxSlots = 65535;          // slot ids fit the uint16 LRU order list
+
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte chunk of a row
+
+// LDS carve-up of one resolve workgroup (byte offsets; every section 16-byte aligned).
+// The hash of the selected ids is dead once hits are found, so the victim list, the
+// missed ids and the per-position gather sources reuse its bytes.
+struct Layout {
+  uint32_t ids, cls, pos_slot, stok, ord, sflag, bitmap, wpre, hash_key, hash_pos, vict, mtok, gsrc, misc;
+  uint32_t hash_bits;  // capacity 2^hash_bits >= 2k
+  uint32_t words;      // miss bitmap words = ceil(H / 32)
+  uint32_t total;
+};
+
+inline uint32_t align16(uint64_t x) { return (uint32_t)((x + 15) & ~uint64_t(15)); }
+
+inline Layout make_layout(int k, int B, int H) {
+  Layout L{};
+  uint32_t bits = 1;
+  while ((1u << bits) < 2u * (uint32_t)k) ++bits;
+  L.hash_bits = bits;
+  const uint64_t hcap = 1ull << bits;
+  L.words = (uint32_t)(((uint64_t)H + 31) / 32);
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) { uint32_t o = (uint32_t)off; off = align16(off + bytes); return o; };
+  L.ids = take(4ull * k);
+  L.cls = take(1ull * k);
+  L.pos_slot = take(4ull * k);
+  L.stok = take(4ull * B);
+  L.ord = take(2ull * B);
+  L.sflag = take(1ull * B);
+  L.bitmap = take(4ull * L.words);
+  L.wpre = take(2ull * L.words);  // uint16 prefix counts (k <= 8192)
+  // hash region, later reused
+  const uint64_t hash_bytes = 8ull * hcap;
+  const uint64_t lists_bytes = 3ull * align16(4ull * k);  // vict, mtok, gsrc
+  const uint32_t region = take(hash_bytes > lists_bytes ? hash_bytes : lists_bytes);
+  L.hash_key = region;
+  L.hash_pos = region + (uint32_t)(4ull * hcap);
+  L.vict = region;
+  L.mtok = region + align16(4ull * k);
+  L.gsrc = L.mtok + align16(4ull * k);
+  L.misc = take(4ull * (4 * kWaves + 8));
+  L.total = (uint32_t)off;
+  return L;
+}
+
+struct ResolveArgs {
+  int32_t R, k, B, H, T, row16;
+  Layout L;
+  const v4u* host;  // device address of the pinned pool [R][H][row16]
+  v4u* hot;         // [R][B][row16]
+  const v4u* tail;  // [R][T][row16]
+  int32_t* slot_tok;
+  int32_t* stamp;
+  uint16_t* order;
+  int32_t* page;
+  int32_t* step;
+  const int32_t* topk;
+  const int32_t* tail0;
+  int32_t* out;
+  int32_t* miss;
+  int32_t* status;
+  v4u* gather;
+};
+
+struct ResetArgs {
+  int32_t R, B, H;
+  const int32_t* ids;  // nullptr: workgroup b resets request b
+  int32_t* slot_tok;
+  int32_t* stamp;
+  uint16_t* order;
+  int32_t* page;
+  int32_t* step;
+};
+
+struct GatherArgs {
+  int32_t R, k, B, T, row16;
+  const int32_t* out;
+  const v4u* hot;
+  const v4u* tail;
+  v4u* gather;
+};
+
+hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s);
+hipError_t launch_reset(const ResetArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+hipError_t set_resolve_lds_limit(uint32_t bytes);
+
+}  // namespace hs

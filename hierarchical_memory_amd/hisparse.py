@@ -1,0 +1,232 @@
+"""Python binding of the HiSparse swap-in C ABI (``include/hisparse.h``).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch supplies device memory and streams. The binding raises if the built
+library is missing; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import json
+import os
+from typing import Any, Dict, Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhisparse.so")
+_lib = None
+
+HS_OK, HS_E_INVALID, HS_E_NOMEM, HS_E_HIP, HS_E_STATE = 0, -1, -2, -3, -4
+HS_STATUS_BAD_ID, HS_STATUS_DUP_ID, HS_STATUS_BAD_STATE = 1, 2, 4
+
+EXPORTED = ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
+            "hs_gather", "hs_destroy", "hs_last_error")
+
+
+class HiSparseError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class HsConfig(ctypes.Structure):
+    _fields_ = [("num_requests", ctypes.c_int32), ("top_k", ctypes.c_int32), ("device_buffer_size", ctypes.c_int32),
+                ("host_to_device_ratio", ctypes.c_float), ("row_bytes", ctypes.c_int32),
+                ("max_context", ctypes.c_int32), ("tail_tokens", ctypes.c_int32)]
+
+
+class HsDeviceViews(ctypes.Structure):
+    _fields_ = [(n, t) for name in ("hot", "tail", "slot_tok", "stamp", "lru_order", "page", "step")
+                for n, t in ((name, ctypes.c_void_p), (name + "_bytes", ctypes.c_uint64))]
+
+
+class HsSizes(ctypes.Structure):
+    _fields_ = [("host_rows", ctypes.c_int32), ("host_pool_bytes", ctypes.c_uint64), ("hot_bytes", ctypes.c_uint64),
+                ("tail_bytes", ctypes.c_uint64), ("slot_tok_bytes", ctypes.c_uint64), ("stamp_bytes", ctypes.c_uint64),
+                ("lru_order_bytes", ctypes.c_uint64), ("page_bytes", ctypes.c_uint64), ("step_bytes", ctypes.c_uint64),
+                ("topk_bytes", ctypes.c_uint64), ("out_bytes", ctypes.c_uint64), ("gather_bytes", ctypes.c_uint64),
+                ("lds_bytes", ctypes.c_uint32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """The loaded HIP library. Raises ImportError when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"libhisparse.so is not built ({_LIB_PATH}); run __graft_entry__.build() or "
+                              "python hierarchical_memory_amd/build.py")
+        # torch ships its own HIP runtime with the same soname; loading torch first makes the library bind
+        # to that one runtime instead of bringing a second one into the process
+        import torch  # noqa: F401
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32 = ctypes.c_void_p, ctypes.c_int32
+        L.hs_required_sizes.argtypes = [ctypes.POINTER(HsConfig), ctypes.POINTER(HsSizes)]
+        L.hs_create.argtypes = [ctypes.POINTER(HsConfig), ctypes.POINTER(vp)]
+        L.hs_host_pool.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(i32)]
+        L.hs_bind_device.argtypes = [vp, ctypes.POINTER(HsDeviceViews)]
+        L.hs_reset.argtypes = [vp, vp, i32, vp]
+        L.hs_resolve.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        L.hs_gather.argtypes = [vp, vp, vp, vp]
+        L.hs_destroy.argtypes = [vp]
+        L.hs_destroy.restype = None
+        L.hs_last_error.argtypes = []
+        L.hs_last_error.restype = ctypes.c_char_p
+        for name in ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
+                     "hs_gather"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def hs_last_error() -> str:
+    return lib().hs_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != HS_OK:
+        raise HiSparseError(rc, hs_last_error())
+
+
+def config(num_requests: int, top_k: int, device_buffer_size: int, host_to_device_ratio: float = 0.0,
+           row_bytes: int = 1152, max_context: int = 0, tail_tokens: int = 0) -> HsConfig:
+    return HsConfig(num_requests, top_k, device_buffer_size, host_to_device_ratio, row_bytes, max_context, tail_tokens)
+
+
+def config_from_hisparse_json(spec: Union[str, Dict[str, Any]], num_requests: int, row_bytes: int = 1152,
+                              max_context: int = 0, tail_tokens: int = 0) -> HsConfig:
+    """Config from the pages' launch option ``--hisparse-config '{"top_k": .., "device_buffer_size": ..,
+    "host_to_device_ratio": ..}'``."""
+    d = json.loads(spec) if isinstance(spec, str) else dict(spec)
+    unknown = set(d) - {"top_k", "device_buffer_size", "host_to_device_ratio"}
+    if unknown:
+        raise ValueError(f"unknown hisparse-config keys: {sorted(unknown)}")
+    return config(num_requests, int(d["top_k"]), int(d["device_buffer_size"]),
+                  float(d.get("host_to_device_ratio", 0.0)), row_bytes, max_context, tail_tokens)
+
+
+def hs_required_sizes(cfg: HsConfig) -> HsSizes:
+    s = HsSizes()
+    _check(lib().hs_required_sizes(ctypes.byref(cfg), ctypes.byref(s)))
+    return s
+
+
+def hs_create(cfg: HsConfig) -> ctypes.c_void_p:
+    ctx = ctypes.c_void_p()
+    _check(lib().hs_create(ctypes.byref(cfg), ctypes.byref(ctx)))
+    return ctx
+
+
+def hs_host_pool(ctx) -> Tuple[int, int, int]:
+    base, stride, rows = ctypes.c_void_p(), ctypes.c_uint64(), ctypes.c_int32()
+    _check(lib().hs_host_pool(ctx, ctypes.byref(base), ctypes.byref(stride), ctypes.byref(rows)))
+    return base.value, stride.value, rows.value
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _bytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def hs_bind_device(ctx, hot, tail, slot_tok, stamp, lru_order, page, step) -> None:
+    v = HsDeviceViews()
+    for name, t in (("hot", hot), ("tail", tail), ("slot_tok", slot_tok), ("stamp", stamp),
+                    ("lru_order", lru_order), ("page", page), ("step", step)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        setattr(v, name, _ptr(t))
+        setattr(v, name + "_bytes", _bytes(t))
+    _check(lib().hs_bind_device(ctx, ctypes.byref(v)))
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def hs_reset(ctx, request_ids=None, stream=None) -> None:
+    n = -1 if request_ids is None else request_ids.numel()
+    _check(lib().hs_reset(ctx, _ptr(request_ids), n, _stream(stream)))
+
+
+def hs_resolve(ctx, topk, tail0, out, miss, status, gather=None, stream=None) -> None:
+    _check(lib().hs_resolve(ctx, _ptr(topk), _ptr(tail0), _ptr(out), _ptr(miss), _ptr(status), _ptr(gather),
+                            _stream(stream)))
+
+
+def hs_gather(ctx, out, gather, stream=None) -> None:
+    _check(lib().hs_gather(ctx, _ptr(out), _ptr(gather), _stream(stream)))
+
+
+def hs_destroy(ctx) -> None:
+    if ctx:
+        lib().hs_destroy(ctx)
+
+
+class SwapIn:
+    """A context plus the torch device tensors it works on (plumbing around the C ABI).
+
+    ``host_pool()`` is a numpy view of the pinned pool, [R, H, row_bytes] uint8, for the caller to fill.
+    """
+
+    def __init__(self, cfg: HsConfig, device: str = "cuda"):
+        import torch
+        self.cfg = cfg
+        self.sizes = hs_required_sizes(cfg)
+        self.R, self.k, self.B = cfg.num_requests, cfg.top_k, cfg.device_buffer_size
+        self.H, self.T, self.rb = self.sizes.host_rows, cfg.tail_tokens, cfg.row_bytes
+        self.device = torch.device(device)
+        self.ctx = hs_create(cfg)
+        dev = self.device
+        self.hot = torch.zeros((self.R, self.B, self.rb), dtype=torch.uint8, device=dev)
+        self.tail = torch.zeros((self.R, self.T, self.rb), dtype=torch.uint8, device=dev) if self.T else None
+        self.slot_tok = torch.empty((self.R, self.B), dtype=torch.int32, device=dev)
+        self.stamp = torch.empty((self.R, self.B), dtype=torch.int32, device=dev)
+        self.lru_order = torch.empty((self.R, self.B), dtype=torch.int16, device=dev)
+        self.page = torch.empty((self.R, self.H), dtype=torch.int32, device=dev)
+        self.step = torch.empty((self.R,), dtype=torch.int32, device=dev)
+        hs_bind_device(self.ctx, self.hot, self.tail, self.slot_tok, self.stamp, self.lru_order, self.page, self.step)
+        hs_reset(self.ctx)
+
+    def host_pool(self) -> np.ndarray:
+        base, stride, rows = hs_host_pool(self.ctx)
+        buf = (ctypes.c_uint8 * (self.R * stride)).from_address(base)
+        return np.frombuffer(buf, dtype=np.uint8).reshape(self.R, rows, self.rb)
+
+    def host_pool_address(self) -> int:
+        return hs_host_pool(self.ctx)[0]
+
+    def reset(self, request_ids=None, stream=None) -> None:
+        hs_reset(self.ctx, request_ids, stream)
+
+    def outputs(self, gather: bool = False):
+        import torch
+        out = torch.empty((self.R, self.k), dtype=torch.int32, device=self.device)
+        miss = torch.empty((self.R,), dtype=torch.int32, device=self.device)
+        status = torch.empty((self.R,), dtype=torch.int32, device=self.device)
+        g = torch.empty((self.R, self.k, self.rb), dtype=torch.uint8, device=self.device) if gather else None
+        return out, miss, status, g
+
+    def resolve(self, topk, tail0=None, gather: bool = False, outputs=None, stream=None):
+        out, miss, status, g = outputs if outputs is not None else self.outputs(gather)
+        hs_resolve(self.ctx, topk, tail0, out, miss, status, g, stream)
+        return out, miss, status, g
+
+    def close(self) -> None:
+        if self.ctx:
+            hs_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,156 @@
+/*
+ * hisparse.h — C ABI of the HiSparse swap-in path on MI355X (gfx950).
+ *
+ * The swap-in step, per request and decode step, as the pages describe it
+ * ("HiSparse: Turbocharging Sparse Attention with Hierarchical Memory",
+ * section 2, the swap-in kernel; 「HiSparse：階層化メモリシステムによる
+ * スパースアテンションの加速」, section 「効率的なSwap-inカーネル」):
+ *   (1) find which of the top-k selected KV tokens miss the hot device buffer,
+ *   (2) choose LRU eviction victims,
+ *   (3) update the page table and fetch the missed rows from host memory.
+ * The hybrid variant ("vLLM GLM 5.3 最適化: Hybrid HiSparse オフローディング",
+ * section 2 Mixed Residency) adds a device-resident tail whose tokens resolve
+ * in place, and a fused gather of every selected row.
+ *
+ * Rules fixed by this library where the pages say only "LRU":
+ *   - eviction candidates are the slots not hit this step, taken in ascending
+ *     (last-use step, slot index); an empty slot has last-use step -1;
+ *   - the j-th smallest missed token id takes the j-th victim;
+ *   - hit slots and newly filled slots get last-use step = the request's step.
+ *
+ * Memory and ownership
+ *   - The library owns the host KV pool: pinned, mapped host memory of
+ *     num_requests x host_rows x row_bytes bytes, request-major. The caller
+ *     fills it (hs_host_pool) before resolving.
+ *   - The caller owns every device buffer (hs_device_views) and the stream.
+ *     Device buffers are plain device pointers; the library checks their sizes
+ *     against the configuration and never frees them.
+ *   - A context is not thread-safe. All device work of a call is enqueued on
+ *     the given stream (NULL = the default stream) and the call returns without
+ *     waiting for it: hs_resolve and hs_gather never synchronise with the host
+ *     and keep the step counters on the device, so a captured HIP graph can
+ *     replay them.
+ *
+ * Errors
+ *   - Every int-returning call returns HS_OK (0) or a negative HS_E_* code
+ *     after synchronous host-side checks; hs_last_error() then describes it.
+ *   - Bad data found on the device (ids out of range, repeated ids, a corrupt
+ *     state table) never traps: it sets bits in the per-request status output
+ *     and the affected entries resolve to -1.
+ */
+#ifndef HISPARSE_H
+#define HISPARSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HS_OK 0
+#define HS_E_INVALID (-1) /* bad argument: null pointer, size out of range, buffer too small, B < k ... */
+#define HS_E_NOMEM (-2)   /* the pinned host pool could not be allocated */
+#define HS_E_HIP (-3)     /* a HIP runtime call failed (no device, launch failure, attribute) */
+#define HS_E_STATE (-4)   /* call out of order (e.g. resolve before hs_bind_device) */
+
+/* Per-request status bits written by hs_resolve. */
+#define HS_STATUS_BAD_ID 1    /* an id outside [0, host_rows), or >= tail0 but outside the tail window */
+#define HS_STATUS_DUP_ID 2    /* an id repeated within the request's selection (first occurrence wins) */
+#define HS_STATUS_BAD_STATE 4 /* the request's slot table or LRU order held an impossible value: nothing
+                                 was changed for this request and every output is -1 */
+
+/*
+ * Configuration. top_k, device_buffer_size and host_to_device_ratio are the
+ * three keys of the HiSparse launch configuration printed on the pages
+ * (「HiSparse：階層化メモリシステムによるスパースアテンションの加速」, section
+ * 「ベンチマークテスト」, and "HiSparse: Turbocharging Sparse Attention with
+ * Hierarchical Memory", section 3 launch scripts: top_k 2048,
+ * device_buffer_size 4096 or 6144, host_to_device_ratio 8 or 10).
+ */
+typedef struct hs_config {
+  int32_t num_requests;       /* R >= 1 */
+  int32_t top_k;              /* k, 1 .. 8192: selected ids per request and step */
+  int32_t device_buffer_size; /* B, k .. 65535: hot slots per request (B >= k so a step never runs out) */
+  float host_to_device_ratio; /* host rows per request = ceil(ratio * B) when max_context == 0 */
+  int32_t row_bytes;          /* bytes per KV row, a positive multiple of 16 (576 bf16 = 1152) */
+  int32_t max_context;        /* > 0: host rows per request (overrides the ratio) */
+  int32_t tail_tokens;        /* T >= 0: device-resident tail rows per request (Mixed residency) */
+} hs_config;
+
+/*
+ * Device buffers (caller-owned). Sizes are in bytes and must be at least what
+ * hs_required_sizes reports; pointers must be 16-byte aligned (hot, tail,
+ * gather output) or 4-byte aligned (tables). H = host rows per request.
+ */
+typedef struct hs_device_views {
+  void* hot;            uint64_t hot_bytes;       /* [R][B][row_bytes] hot buffer rows */
+  void* tail;           uint64_t tail_bytes;      /* [R][T][row_bytes] resident tail rows; NULL when T == 0 */
+  int32_t* slot_tok;    uint64_t slot_tok_bytes;  /* [R][B] token held by each slot, -1 = empty */
+  int32_t* stamp;       uint64_t stamp_bytes;     /* [R][B] last-use step of each slot, -1 = empty */
+  uint16_t* lru_order;  uint64_t lru_order_bytes; /* [R][B] slots in ascending (stamp, slot) (library-maintained) */
+  int32_t* page;        uint64_t page_bytes;      /* [R][H] slot of each token, -1 = not in the hot buffer */
+  int32_t* step;        uint64_t step_bytes;      /* [R] step counter of each request */
+} hs_device_views;
+
+typedef struct hs_sizes {
+  int32_t host_rows;         /* H */
+  uint64_t host_pool_bytes;  /* R * H * row_bytes */
+  uint64_t hot_bytes, tail_bytes, slot_tok_bytes, stamp_bytes, lru_order_bytes, page_bytes, step_bytes;
+  uint64_t topk_bytes;       /* [R][k] int32 input of one step */
+  uint64_t out_bytes;        /* [R][k] int32 output of one step */
+  uint64_t gather_bytes;     /* [R][k][row_bytes] gather output */
+  uint32_t lds_bytes;        /* LDS one resolve workgroup uses */
+} hs_sizes;
+
+typedef struct hs_ctx hs_ctx;
+
+/* Sizes every buffer needs for cfg. Host-only; validates cfg like hs_create. */
+int hs_required_sizes(const hs_config* cfg, hs_sizes* out);
+
+/* Validate cfg, allocate the pinned mapped host pool on the current HIP device
+ * (contents undefined until the caller fills it) and return a context. */
+int hs_create(const hs_config* cfg, hs_ctx** out);
+
+/* Host address of the pool: request r's row x starts at
+ * host_base + r * request_stride_bytes + x * row_bytes. */
+int hs_host_pool(hs_ctx* ctx, void** host_base, uint64_t* request_stride_bytes, int32_t* host_rows);
+
+/* Register the caller's device buffers (checked against the sizes). Must precede reset/resolve/gather. */
+int hs_bind_device(hs_ctx* ctx, const hs_device_views* views);
+
+/* Reset requests to the empty state: slot table, stamps and page table -1, LRU order = slot order,
+ * step 0. Hot rows are left as they are. d_request_ids: device int32[n]; NULL with n < 0 resets all.
+ * Ids outside [0, R) are skipped. */
+int hs_reset(hs_ctx* ctx, const int32_t* d_request_ids, int32_t n, void* stream);
+
+/*
+ * One decode step for every request (one workgroup per request).
+ *   d_topk    [R][k] int32: selected token ids; -1 = padding.
+ *   d_tail0   [R] int32 or NULL: first device-resident token of each request; a token x with
+ *             tail0 <= x < tail0 + T resolves to B + (x - tail0) and takes no slot.
+ *   d_out     [R][k] int32: slot of each id (hit or newly filled), B + tail index for a resident id,
+ *             -1 for padding or a bad id.
+ *   d_miss    [R] int32: misses (rows fetched from the host pool) of each request.
+ *   d_status  [R] int32: HS_STATUS_* bits of this step.
+ *   d_gather  [R][k][row_bytes] or NULL: when given, row i of request r receives the row d_out names
+ *             (hot slot, tail row, or the fetched row); zeros for -1 (fused resolve + gather).
+ * Inputs must not alias outputs or state.
+ */
+int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
+               int32_t* d_status, void* d_gather, void* stream);
+
+/* Unfused gather: d_gather[r][i] = the row d_out[r][i] names (as in hs_resolve), zeros for -1 or for
+ * an index outside [0, B + T). d_out [R][k] int32, d_gather [R][k][row_bytes]. */
+int hs_gather(hs_ctx* ctx, const int32_t* d_out, void* d_gather, void* stream);
+
+/* Free the host pool and the context (device buffers belong to the caller). NULL is ignored. */
+void hs_destroy(hs_ctx* ctx);
+
+/* Message of the last failing call in this thread ("" if none). */
+const char* hs_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HISPARSE_H */

@@ -1,0 +1,90 @@
+"""The C ABI without a GPU: the library loads, exports what include/hisparse.h declares, and rejects bad
+configurations with an error code and a message before touching the device."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import hierarchical_memory_amd as hm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hisparse.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|void|const char\*)\s+(hs_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 9
+    lib = ctypes.CDLL(hm.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(hm.EXPORTED)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(num_requests=0), "num_requests"),
+    (dict(top_k=0), "top_k"),
+    (dict(top_k=9000, device_buffer_size=9000), "top_k"),
+    (dict(device_buffer_size=100), "device_buffer_size"),
+    (dict(device_buffer_size=70000), "device_buffer_size"),
+    (dict(row_bytes=1000), "row_bytes"),
+    (dict(row_bytes=0), "row_bytes"),
+    (dict(host_to_device_ratio=0.0), "host_to_device_ratio"),
+    (dict(host_to_device_ratio=-1.0), "host_to_device_ratio"),
+    (dict(tail_tokens=-1), "tail_tokens"),
+    (dict(max_context=-5), "max_context"),
+    (dict(device_buffer_size=40000, max_context=1 << 20), "LDS"),
+])
+def test_bad_config_rejected(kw, msg):
+    base = dict(num_requests=4, top_k=256, device_buffer_size=512, host_to_device_ratio=8.0, row_bytes=1152,
+                max_context=0, tail_tokens=0)
+    base.update(kw)
+    cfg = hm.HsConfig(**base)
+    with pytest.raises(hm.HiSparseError) as e:
+        hm.hs_required_sizes(cfg)
+    assert e.value.code == hm.HS_E_INVALID and msg in str(e.value)
+    with pytest.raises(hm.HiSparseError):
+        hm.hs_create(cfg)  # fails in the same host-side check, before any HIP call
+
+
+def test_null_arguments():
+    lib = hm.lib()
+    assert lib.hs_required_sizes(None, None) == hm.HS_E_INVALID
+    assert lib.hs_create(None, None) == hm.HS_E_INVALID
+    assert lib.hs_resolve(None, None, None, None, None, None, None, None) == hm.HS_E_INVALID
+    assert lib.hs_reset(None, None, -1, None) == hm.HS_E_INVALID
+    assert lib.hs_gather(None, None, None, None) == hm.HS_E_INVALID
+    assert lib.hs_bind_device(None, None) == hm.HS_E_INVALID
+    assert "NULL" in hm.hs_last_error()
+    lib.hs_destroy(None)
+
+
+def test_launch_configs_from_the_pages():
+    lines = [l for l in open(os.path.join(GOLDEN, "hisparse_launch_configs.txt")) if l.startswith("{")]
+    got = []
+    for l in lines:
+        cfg = hm.config_from_hisparse_json(l.strip(), num_requests=32)
+        s = hm.hs_required_sizes(cfg)
+        got.append((cfg.top_k, cfg.device_buffer_size, s.host_rows))
+    # host rows = ratio x buffer slots
+    assert got == [(2048, 6144, 61440), (2048, 4096, 32768)]
+    with pytest.raises(ValueError):
+        hm.config_from_hisparse_json('{"top_k": 1, "device_buffer": 2}', 1)
+
+
+def test_sizes_of_the_workloads():
+    import workload
+    for w in workload.ALL:
+        s = hm.hs_required_sizes(hm.config(w.num_requests, w.top_k, w.buffer_slots, 0.0, w.row_bytes, w.host_rows,
+                                           w.tail_tokens))
+        assert s.host_rows == w.host_rows
+        assert s.host_pool_bytes == w.num_requests * w.host_rows * w.row_bytes
+        assert s.lds_bytes <= 159 * 1024
+        assert s.hot_bytes == w.num_requests * w.buffer_slots * w.row_bytes

@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, bit for bit.
+
+Every output (slots, miss counts, status), every table (slot table, stamps, page table, step counters), the
+hot buffer's bytes and the gathered rows must equal the oracle's. Nothing here has a floating-point
+tolerance: rows are copied, not computed.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import hierarchical_memory_amd  # noqa: F401  (raises if the HIP library is missing)
+    yield
+    torch.cuda.synchronize()
+
+
+import workload  # noqa: E402
+from tests.parity import Pair, log  # noqa: E402
+
+
+def _random_ids(rng, R, steps, k, H, extra_low=-3, extra_high=3, p_weird=0.1):
+    """Random selections, mostly valid distinct ids, sometimes padding, out-of-range or repeated ids."""
+    ids = np.empty((R, steps, k), np.int32)
+    for r in range(R):
+        for t in range(steps):
+            row = rng.choice(H, size=k, replace=k > H).astype(np.int32) if H >= 1 else np.zeros(k, np.int32)
+            weird = rng.random(k) < p_weird
+            row[weird] = rng.integers(extra_low, H + extra_high, size=int(weird.sum()))
+            ids[r, t] = row
+    return ids
+
+
+TINY = [  # (k, B, H, T, row_bytes)
+    (1, 1, 3, 0, 16), (2, 3, 6, 0, 16), (3, 4, 6, 0, 48), (3, 3, 5, 2, 16), (7, 9, 30, 0, 32),
+    (12, 20, 40, 6, 16), (33, 40, 100, 0, 1152), (64, 64, 200, 0, 64), (65, 130, 257, 17, 80),
+]
+
+
+@pytest.mark.parametrize("k,B,H,T,rb", TINY, ids=[f"k{k}_B{B}_H{H}_T{T}_rb{rb}" for k, B, H, T, rb in TINY])
+def test_tiny_random(k, B, H, T, rb):
+    rng = np.random.default_rng(k * 1000 + B)
+    R, steps = 16, 12
+    w = workload.SINGLE_4K.with_(name=f"tiny_k{k}_B{B}", num_requests=R, top_k=k, buffer_slots=B, host_rows=H,
+                                 L0=H, tail_tokens=T, row_elems=rb // 2, steps=steps, fused_gather=True)
+    ids = _random_ids(rng, R, steps, k, H)
+    tail0 = rng.integers(0, H + 1, size=R).astype(np.int32) if T else None
+    p = Pair(w, ids=ids, tail0=tail0, gather=True)
+    p.run(check_every=1)
+    p.close()
+
+
+def test_single_request_full():
+    p = Pair(workload.SINGLE_4K, gather=True)
+    p.run(check_every=1)
+    p.close()
+
+
+def test_grow_32_requests_full():
+    p = Pair(workload.GROW_32)
+    p.run(check_every=16)
+    p.check_all_requests()
+    p.close()
+
+
+@pytest.mark.parametrize("w", workload.sweep_workloads(), ids=lambda w: w.name)
+def test_buffer_sweep(w):
+    p = Pair(w, sample=[0, 21, 42, 63])
+    p.run(check_every=64)
+    p.check_all_requests(rows_per_request=16)
+    p.close()
+
+
+def test_concurrency_256_requests_full():
+    p = Pair(workload.CONC_256, sample=[0, 85, 170, 255])
+    p.run(check_every=64)
+    p.check_all_requests(rows_per_request=16)
+    p.close()
+
+
+def test_hybrid_tail_fused_gather_full():
+    p = Pair(workload.HYBRID_64, sample=[0, 31, 63])
+    p.run(check_every=32)
+    p.check_all_requests(rows_per_request=16)
+    p.close()
+
+
+def test_unfused_gather_matches_fused():
+    import hierarchical_memory_amd as hm
+    w = workload.HYBRID_64.with_(num_requests=8, steps=6)
+    p = Pair(w, sample=[0, 7], gather=True)
+    for _ in range(w.steps):
+        p.step()
+        out, _, _, g = p.outs
+        g2 = torch.empty_like(g)
+        hm.hs_gather(p.sw.ctx, out, g2)
+        assert torch.equal(g, g2)
+    p.close()
+
+
+def test_buffer_equals_topk_and_whole_context():
+    """B = k (every free slot shares the previous step's stamp) and B >= context (compulsory misses only)."""
+    for B in (256, 4096):
+        p = Pair(workload.SINGLE_4K.with_(buffer_slots=B))
+        p.run(check_every=8)
+        p.close()
+
+
+def test_run_twice_identical():
+    outs = []
+    for _ in range(2):
+        p = Pair(workload.GROW_32.with_(num_requests=8, steps=24), sample=[3])
+        res = []
+        for _ in range(p.n_steps):
+            p.step()
+            res.append(p.outs[0].cpu().numpy().copy())
+        res.append(p.sw.stamp.cpu().numpy())
+        res.append(p.sw.hot.cpu().numpy())
+        outs.append(res)
+        p.close()
+    for a, b in zip(*outs):
+        assert (a == b).all()
+
+
+def test_partial_reset_mid_run():
+    import hierarchical_memory_amd as hm
+    w = workload.GROW_32.with_(num_requests=6, steps=20)
+    p = Pair(w)
+    for t in range(w.steps):
+        if t == 9:
+            ids = torch.tensor([1, 4, 99, -1], dtype=torch.int32, device="cuda")  # 99 and -1 are skipped
+            hm.hs_reset(p.sw.ctx, ids)
+            p.o.reset([1, 4])
+            p.check_state()
+        p.step(check_state=True)
+    p.close()
+
+
+def test_padding_bad_and_repeated_ids():
+    w = workload.SINGLE_4K.with_(num_requests=4, top_k=16, buffer_slots=20, host_rows=50, L0=50, steps=6)
+    ids = np.array([[[3, 3, -1, 60, -5, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16, 17]] * 6] * 4, np.int32)
+    ids[1] = -1
+    ids[2, :, 0] = 49
+    p = Pair(w, ids=ids)
+    p.run(check_every=1)
+    st = p.outs[2].cpu().numpy()
+    assert st.tolist() == [3, 0, 1, 3]
+    p.close()
+
+
+def test_corrupt_state_is_reported_not_used():
+    import hierarchical_memory_amd as hm
+    w = workload.SINGLE_4K.with_(num_requests=3, steps=4)
+    p = Pair(w, sample=[0, 2])
+    p.step()
+    # corrupt request 1's slot table from the host: the kernel must refuse it and leave its state alone
+    p.sw.slot_tok[1, 5] = w.host_rows + 7
+    before = [t.clone() for t in (p.sw.slot_tok, p.sw.stamp, p.sw.page, p.sw.step, p.sw.hot)]
+    p.step()
+    out, miss, status, _ = p.outs
+    assert status[1].item() == hm.HS_STATUS_BAD_STATE and miss[1].item() == 0 and (out[1] == -1).all()
+    for b, a in zip(before, (p.sw.slot_tok, p.sw.stamp, p.sw.page, p.sw.step, p.sw.hot)):
+        assert torch.equal(b[1], a[1])
+    p.check_state()
+    p.close()
+
+
+def test_graph_replay_equals_eager():
+    """The resolve never waits on the host and keeps its step counter on the device, so a captured graph
+    replays it; every replay must equal an eager run on the same inputs."""
+    w = workload.GROW_32.with_(num_requests=4, steps=10)
+    eager = Pair(w, sample=[])
+    graph = Pair(w, sample=[0, 1, 2, 3])
+    topk = torch.empty((w.num_requests, w.top_k), dtype=torch.int32, device="cuda")
+    g_out = graph.sw.outputs(False)
+    # warm up on a side stream, then capture one resolve
+    topk.copy_(torch.from_numpy(np.ascontiguousarray(graph.ids[:, 0])))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg, stream=s):
+        graph.sw.resolve(topk, None, False, outputs=g_out)
+    torch.cuda.synchronize()
+    for t in range(w.steps):
+        topk.copy_(torch.from_numpy(np.ascontiguousarray(graph.ids[:, t])))
+        cg.replay()
+        torch.cuda.synchronize()
+        eager.step()
+        e_out = eager.outs[0]
+        assert torch.equal(g_out[0], e_out) and torch.equal(g_out[1], eager.outs[1])
+        # and the oracle agrees with the replay
+        o_out, o_miss, _, _ = graph.o.step(graph.ids[:, t])
+        assert (g_out[0].cpu().numpy() == o_out).all()
+        graph.t += 1
+    graph.check_state()
+    for name in ("slot_tok", "stamp", "page", "step", "hot"):
+        assert torch.equal(getattr(graph.sw, name), getattr(eager.sw, name)), name
+    eager.close()
+    graph.close()
+
+
+def test_largest_shape_that_fits_lds():
+    """Near the LDS limit of one workgroup: a wide buffer and a long context."""
+    import hierarchical_memory_amd as hm
+    cfg = hm.config(2, 2048, 8192, 0.0, 1152, 200000)
+    s = hm.hs_required_sizes(cfg)
+    assert s.lds_bytes > 128 * 1024
+    w = workload.SINGLE_4K.with_(name="wide", num_requests=2, top_k=2048, buffer_slots=8192, host_rows=200000,
+                                 L0=200000, window=20000, steps=10)
+    p = Pair(w)
+    p.run(check_every=3)
+    p.close()
