@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true")
+    ap.add_argument("--split-steps", type=int, default=-1,
+                    help="steps of the plan+copy leg after a reset (default: the same warmup+steps)")
     return ap.parse_args()
 
 
@@ -102,6 +104,50 @@ def cpu_baseline(w, ids, seconds: float):
     return {"value": entries / dt, "unit": "entries/s", "cores": 1, "kind": "oracle",
             "sample": f"{n_req} of {w.num_requests} requests x all {n_steps} steps ({dt:.1f} s, single thread)",
             "miss_copy_GBps": misses * w.row_bytes / dt / 1e9}
+
+
+def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step):
+    """The same stream again from a reset, as hs_plan + hs_copy on one stream. The plan kernel carries all the
+    metadata work of a step (hit test, ranks, victims, page/slot tables, stamps, outputs) and no rows, so its
+    duration prices the hit path against HBM."""
+    R, k, B, rb = w.num_requests, w.top_k, w.buffer_slots, w.row_bytes
+    stream = torch.cuda.current_stream()
+    sw.reset()
+    plan = sw.plan_buffer()
+    out = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    miss = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
+    status = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
+    for t in range(W):
+        hm.hs_plan(sw.ctx, topk[t], tail0, out, miss[t], status[t], plan, stream)
+        hm.hs_copy(sw.ctx, plan, miss[t], stream)
+    torch.cuda.synchronize()
+    ea = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    eb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for i in range(K):
+        ea[i].record(stream)
+        hm.hs_plan(sw.ctx, topk[W + i], tail0, out, miss[W + i], status[W + i], plan, stream)
+        eb[i].record(stream)
+        hm.hs_copy(sw.ctx, plan, miss[W + i], stream)
+    ea[K].record(stream)
+    torch.cuda.synchronize()
+    plan_ms = np.array([ea[i].elapsed_time(eb[i]) for i in range(K)])
+    copy_ms = np.array([eb[i].elapsed_time(ea[i + 1]) for i in range(K)])
+    total_ms = ea[0].elapsed_time(ea[K])
+    m = miss[W:].cpu().numpy().astype(np.int64)
+    if status[W:].cpu().numpy().any():
+        raise SystemExit("device status bits set during the split leg")
+    mean_m = m.sum() / K
+    meta = R * (12 * k + 8 * B) + 12 * mean_m
+    plan_avg = float(plan_ms.mean())
+    hit_gbps = meta / (plan_avg / 1e3) / 1e9
+    copy_gbps = mean_m * rb / (float(copy_ms.mean()) / 1e3) / 1e9
+    log(f"[bench] split: plan {plan_avg * 1e3:.1f} us/step ({hit_gbps:.0f} GB/s of metadata), copy "
+        f"{copy_ms.mean() * 1e3:.0f} us/step ({copy_gbps:.1f} GB/s), whole step {total_ms / K:.3f} ms")
+    return {"kernel": "resolve_kernel<plan> (hs_plan)", "bound": "hbm", "achieved": hit_gbps, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": hit_gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": meta,
+            "avg_launch_us": plan_avg * 1e3, "p50_launch_us": float(np.median(plan_ms)) * 1e3,
+            "copy_kernel_avg_us": float(copy_ms.mean()) * 1e3, "copy_kernel_GBps": copy_gbps,
+            "split_step_ms": total_ms / K, "same_misses_as_fused": bool(abs(mean_m - mean_miss_per_step) < 1e-6)}
 
 
 def main() -> int:
@@ -214,6 +260,9 @@ def main() -> int:
         "hbm": {"achieved": hbm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hbm_gbps / HBM_PEAK_GBPS,
                 "algorithmic_bytes_per_launch": hbm_bytes},
     }
+    if args.split_steps != 0:
+        rep["hit_path"] = split_leg(hm, torch, np, sw, topk, tail0, W, K if args.split_steps < 0 else args.split_steps,
+                                    w, total_miss / K)
     sw.close()
     del topk
     if not args.no_cpu_baseline:

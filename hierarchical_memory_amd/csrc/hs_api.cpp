@@ -44,7 +44,8 @@ int hip_fail(hipError_t e, const char* what) {
 // Validates cfg and derives the host rows and LDS layout. Host-only.
 int check_config(const hs_config* cfg, int32_t* H_out, hs::Layout* L_out) {
   if (!cfg) return fail(HS_E_INVALID, "config is NULL");
-  if (cfg->num_requests < 1) return fail(HS_E_INVALID, "num_requests must be >= 1 (got %d)", cfg->num_requests);
+  if (cfg->num_requests < 1 || cfg->num_requests > 65535)
+    return fail(HS_E_INVALID, "num_requests must be in [1, 65535] (got %d)", cfg->num_requests);
   if (cfg->top_k < 1 || cfg->top_k > hs::kMaxTopK)
     return fail(HS_E_INVALID, "top_k must be in [1, %d] (got %d)", hs::kMaxTopK, cfg->top_k);
   if (cfg->device_buffer_size < cfg->top_k || cfg->device_buffer_size > hs::kMaxSlots)
@@ -90,6 +91,7 @@ void fill_sizes(const hs_config* cfg, int32_t H, const hs::Layout& L, hs_sizes* 
   s->topk_bytes = R * k * 4;
   s->out_bytes = R * k * 4;
   s->gather_bytes = R * k * rb;
+  s->plan_bytes = R * 2 * k * 4;
   s->lds_bytes = L.total;
 }
 
@@ -131,7 +133,7 @@ int hs_create(const hs_config* cfg, hs_ctx** out) {
   if ((int64_t)L.total + 1024 > (int64_t)lds_max)
     return fail(HS_E_INVALID, "this shape needs %u bytes of LDS per workgroup, the device allows %d", L.total,
                 lds_max);
-  e = hs::set_resolve_lds_limit(L.total);
+  e = hs::set_lds_limits(L.total, 4u * (uint32_t)cfg->device_buffer_size);
   if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(resolve kernel LDS)");
 
   hs_ctx* ctx = new (std::nothrow) hs_ctx();
@@ -230,8 +232,12 @@ int hs_reset(hs_ctx* ctx, const int32_t* d_request_ids, int32_t n, void* stream)
   return ok();
 }
 
-int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
-               int32_t* d_status, void* d_gather, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int resolve_common(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
+                   int32_t* d_status, void* d_gather, int32_t* d_plan, void* stream) {
   int rc = check_ready(ctx);
   if (rc) return rc;
   if (!d_topk || !d_out || !d_miss || !d_status)
@@ -261,8 +267,43 @@ int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32
   a.miss = d_miss;
   a.status = d_status;
   a.gather = (hs::v4u*)d_gather;
+  a.plan = d_plan;
   hipError_t e = hs::launch_resolve(a, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "resolve launch");
+  if (e != hipSuccess) return hip_fail(e, d_plan ? "plan launch" : "resolve launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
+               int32_t* d_status, void* d_gather, void* stream) {
+  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, d_gather, nullptr, stream);
+}
+
+int hs_plan(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
+            int32_t* d_status, int32_t* d_plan, void* stream) {
+  if (!d_plan) return fail(HS_E_INVALID, "plan buffer must not be NULL");
+  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, nullptr, d_plan, stream);
+}
+
+int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* stream) {
+  int rc = check_ready(ctx);
+  if (rc) return rc;
+  if (!d_plan || !d_miss) return fail(HS_E_INVALID, "plan and miss must not be NULL");
+  hs::CopyArgs a{};
+  a.R = ctx->cfg.num_requests;
+  a.k = ctx->cfg.top_k;
+  a.B = ctx->cfg.device_buffer_size;
+  a.H = ctx->H;
+  a.row16 = ctx->cfg.row_bytes / 16;
+  a.plan = d_plan;
+  a.miss = d_miss;
+  a.host = (const hs::v4u*)ctx->pool_dev;
+  a.hot = (hs::v4u*)ctx->views.hot;
+  hipError_t e = hs::launch_copy(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "copy launch");
   return ok();
 }
 
@@ -283,6 +324,19 @@ int hs_gather(hs_ctx* ctx, const int32_t* d_out, void* d_gather, void* stream) {
   a.gather = (hs::v4u*)d_gather;
   hipError_t e = hs::launch_gather(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+int hs_rebuild_order(hs_ctx* ctx, void* stream) {
+  int rc = check_ready(ctx);
+  if (rc) return rc;
+  hs::RebuildArgs a{};
+  a.R = ctx->cfg.num_requests;
+  a.B = ctx->cfg.device_buffer_size;
+  a.stamp = ctx->views.stamp;
+  a.order = ctx->views.lru_order;
+  hipError_t e = hs::launch_rebuild_order(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rebuild-order launch");
   return ok();
 }
 

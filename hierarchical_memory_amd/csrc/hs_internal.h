@@ -73,6 +73,21 @@ struct ResolveArgs {
   int32_t* miss;
   int32_t* status;
   v4u* gather;
+  int32_t* plan;    // non-null: plan-only launch, [R][2][k] (missed tokens, then their victim slots)
+};
+
+struct CopyArgs {
+  int32_t R, k, B, H, row16;
+  const int32_t* plan;  // [R][2][k]
+  const int32_t* miss;  // [R]
+  const v4u* host;
+  v4u* hot;
+};
+
+struct RebuildArgs {
+  int32_t R, B;
+  const int32_t* stamp;
+  uint16_t* order;
 };
 
 struct ResetArgs {
@@ -96,6 +111,8 @@ struct GatherArgs {
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s);
 hipError_t launch_reset(const ResetArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
-hipError_t set_resolve_lds_limit(uint32_t bytes);
+hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
+hipError_t launch_rebuild_order(const RebuildArgs& a, hipStream_t s);
+hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes);
 
 }  // namespace hs

@@ -74,6 +74,9 @@ __device__ __forceinline__ v4u load_host(const v4u* p) { return __builtin_nontem
 
 }  // namespace
 
+// kPlanOnly: stop after phase 5 and write the miss list (token, victim slot) to a.plan instead of
+// copying rows; copy_kernel then moves the rows, possibly on another stream.
+template <bool kPlanOnly>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Layout& L = a.L;
@@ -272,7 +275,12 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       a.page[rH + x] = v;
       a.slot_tok[rB + v] = x;
       a.stamp[rB + v] = t;
-      mtok[j] = x;
+      if (kPlanOnly) {
+        a.plan[rk * 2 + j] = x;
+        a.plan[rk * 2 + a.k + j] = v;
+      } else {
+        mtok[j] = x;
+      }
       o = v;
       g = -2 - j;
     } else if (c == C_HIT) {
@@ -309,6 +317,15 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       if (f && pos < B) a.order[rB + pos] = (uint16_t)s;  // pos < B always holds for a permutation
       run += __popcll(mask);
     }
+  }
+
+  if (kPlanOnly) {
+    if (tid == 0) {
+      a.step[r] = t + 1;
+      a.miss[r] = m;
+      a.status[r] = misc[kMiscStatus];
+    }
+    return;
   }
 
   // ---- phase 6: rows
@@ -407,12 +424,91 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
   }
 }
 
-hipError_t set_resolve_lds_limit(uint32_t bytes) {
-  return hipFuncSetAttribute((const void*)resolve_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+// Rows of a plan: workgroup (g, r) copies every gridDim.x-th group of 16-byte chunks of request r's
+// missed rows from the pinned host pool into their victim slots.
+__global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
+  const int r = blockIdx.y;
+  const int m = a.miss[r];
+  if (m <= 0 || m > a.k) return;
+  const int row16 = a.row16;
+  const int total = m * row16;
+  const size_t rk = (size_t)r * a.k;
+  const int32_t* ptok = a.plan + rk * 2;
+  const int32_t* pslot = ptok + a.k;
+  const v4u* hostr = a.host + (size_t)r * a.H * row16;
+  v4u* hotr = a.hot + (size_t)r * a.B * row16;
+  const int stride = gridDim.x * blockDim.x;
+  for (int c0 = blockIdx.x * blockDim.x + threadIdx.x; c0 < total; c0 += stride * kUnroll) {
+    v4u v[kUnroll];
+    long long dst[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = c0 + u * stride;
+      dst[u] = -1;
+      if (c < total) {
+        const int j = c / row16, q = c - j * row16;
+        const int x = ptok[j], s = pslot[j];
+        if (x >= 0 && x < a.H && s >= 0 && s < a.B) {
+          v[u] = load_host(hostr + (size_t)x * row16 + q);
+          dst[u] = (long long)s * row16 + q;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (dst[u] >= 0) hotr[dst[u]] = v[u];
+  }
+}
+
+// Rebuilds request r's LRU order list from its stamps: the rank of slot s is the number of slots with a
+// smaller (stamp, slot) key, counted against all B stamps staged in LDS. Used after a caller imports
+// tables that did not carry the order list; O(B^2 / 1024) per thread, off the decode path.
+__global__ __launch_bounds__(1024) void rebuild_order_kernel(RebuildArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  int32_t* st = (int32_t*)smem;
+  const int r = blockIdx.x;
+  const size_t rB = (size_t)r * a.B;
+  for (int s = threadIdx.x; s < a.B; s += blockDim.x) st[s] = a.stamp[rB + s];
+  __syncthreads();
+  for (int s = threadIdx.x; s < a.B; s += blockDim.x) {
+    const int32_t mine = st[s];
+    int rank = 0;
+    for (int u = 0; u < a.B; ++u) {
+      const int32_t o = st[u];
+      rank += (o < mine) || (o == mine && u < s);
+    }
+    a.order[rB + rank] = (uint16_t)s;
+  }
+}
+
+hipError_t launch_rebuild_order(const RebuildArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(rebuild_order_kernel, dim3(a.R), dim3(1024), (size_t)a.B * 4, s, a);
+  return hipGetLastError();
+}
+
+hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes) {
+  hipError_t e = hipFuncSetAttribute((const void*)resolve_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)resolve_bytes);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)resolve_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)resolve_bytes);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)rebuild_order_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)rebuild_bytes);
 }
 
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(resolve_kernel, dim3(a.R), dim3(kThreads), a.L.total, s, a);
+  if (a.plan) hipLaunchKernelGGL(resolve_kernel<true>, dim3(a.R), dim3(kThreads), a.L.total, s, a);
+  else hipLaunchKernelGGL(resolve_kernel<false>, dim3(a.R), dim3(kThreads), a.L.total, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
+  // about 2048 workgroups over the whole chip whatever the number of requests
+  int g = (2048 + a.R - 1) / a.R;
+  if (g < 1) g = 1;
+  if (g > 64) g = 64;
+  hipLaunchKernelGGL(copy_kernel, dim3(g, a.R), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -68,7 +68,7 @@ extern "C" {
  * device_buffer_size 4096 or 6144, host_to_device_ratio 8 or 10).
  */
 typedef struct hs_config {
-  int32_t num_requests;       /* R >= 1 */
+  int32_t num_requests;       /* R, 1 .. 65535 */
   int32_t top_k;              /* k, 1 .. 8192: selected ids per request and step */
   int32_t device_buffer_size; /* B, k .. 65535: hot slots per request (B >= k so a step never runs out) */
   float host_to_device_ratio; /* host rows per request = ceil(ratio * B) when max_context == 0 */
@@ -99,6 +99,7 @@ typedef struct hs_sizes {
   uint64_t topk_bytes;       /* [R][k] int32 input of one step */
   uint64_t out_bytes;        /* [R][k] int32 output of one step */
   uint64_t gather_bytes;     /* [R][k][row_bytes] gather output */
+  uint64_t plan_bytes;       /* [R][2][k] int32 miss list of hs_plan */
   uint32_t lds_bytes;        /* LDS one resolve workgroup uses */
 } hs_sizes;
 
@@ -139,9 +140,30 @@ int hs_reset(hs_ctx* ctx, const int32_t* d_request_ids, int32_t n, void* stream)
 int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
                int32_t* d_status, void* d_gather, void* stream);
 
+/*
+ * The same step split in two, so the row copy can overlap other work: the pages name better overlap of
+ * the swap-in I/O as the way to cut its cost ("HiSparse: Turbocharging Sparse Attention with Hierarchical
+ * Memory", section 4 future work; 「HiSparse：階層化メモリシステムによるスパースアテンションの加速」, section
+ * 「今後の展望」).
+ * hs_plan does everything hs_resolve does except moving rows: outputs, page table, slot table, stamps and
+ * step counters are final when it completes; d_plan [R][2][k] int32 receives, for request r, the missed
+ * tokens in ascending id order (d_plan[r][0][0..m)) and their slots (d_plan[r][1][0..m)).
+ * hs_copy then copies those rows from the host pool into the hot buffer. Until it completes, the hot rows
+ * of this step's new slots are stale. Two plans may run back to back, but the copy of a step must complete
+ * before the copy of the next step and before anything reads the hot rows.
+ */
+int hs_plan(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
+            int32_t* d_status, int32_t* d_plan, void* stream);
+int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* stream);
+
 /* Unfused gather: d_gather[r][i] = the row d_out[r][i] names (as in hs_resolve), zeros for -1 or for
  * an index outside [0, B + T). d_out [R][k] int32, d_gather [R][k][row_bytes]. */
 int hs_gather(hs_ctx* ctx, const int32_t* d_out, void* d_gather, void* stream);
+
+/* Rebuild every request's LRU order list from its stamps (ascending (stamp, slot)). Call it after
+ * writing slot_tok / stamp / page / step from a snapshot that did not carry lru_order; a snapshot of all
+ * seven device buffers restores without it. */
+int hs_rebuild_order(hs_ctx* ctx, void* stream);
 
 /* Free the host pool and the context (device buffers belong to the caller). NULL is ignored. */
 void hs_destroy(hs_ctx* ctx);

@@ -218,3 +218,113 @@ def test_largest_shape_that_fits_lds():
     p = Pair(w)
     p.run(check_every=3)
     p.close()
+
+
+def _check_plan(plan_r, out_r, ids_r, m):
+    """The plan lists the step's missed ids in ascending order with the slots they were given."""
+    toks = plan_r[0][:m]
+    assert (np.diff(toks) > 0).all() if m > 1 else True
+    pos = {int(x): i for i, x in enumerate(ids_r)}
+    assert [int(out_r[pos[int(x)]]) for x in toks] == plan_r[1][:m].tolist()
+
+
+def test_plan_then_copy_matches_oracle():
+    import hierarchical_memory_amd as hm
+    w = workload.GROW_32.with_(num_requests=8, steps=40)
+    p = Pair(w, sample=[0, 5, 7])
+    plan = p.sw.plan_buffer()
+    out, miss, status, _ = p.outs
+    for t in range(w.steps):
+        ids = p.ids[:, t]
+        topk = torch.from_numpy(np.ascontiguousarray(ids)).cuda()
+        hm.hs_plan(p.sw.ctx, topk, None, out, miss, status, plan)
+        hm.hs_copy(p.sw.ctx, plan, miss)
+        o_out, o_miss, o_status, _ = p.o.step(ids[p.sample])
+        s = p.sample_t
+        assert (out[s].cpu().numpy() == o_out).all() and (miss[s].cpu().numpy() == o_miss).all()
+        assert (status[s].cpu().numpy() == o_status).all()
+        pl, oc, mc = plan.cpu().numpy(), out.cpu().numpy(), miss.cpu().numpy()
+        for r in range(w.num_requests):
+            _check_plan(pl[r], oc[r], ids[r], int(mc[r]))
+        p.t += 1
+        if t % 8 == 0 or t == w.steps - 1:
+            p.check_state()
+    p.close()
+
+
+def test_copy_overlapped_on_second_stream():
+    """Plans on the main stream, copies on a second stream, two steps in flight with double-buffered plans;
+    after the last copy every table and every hot row equals the oracle's."""
+    import hierarchical_memory_amd as hm
+    w = workload.GROW_32.with_(num_requests=8, steps=30)
+    p = Pair(w, sample=list(range(8)))
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    plans = [p.sw.plan_buffer() for _ in range(2)]
+    misses = [torch.empty((w.num_requests,), dtype=torch.int32, device="cuda") for _ in range(2)]
+    out, _, status, _ = p.outs
+    copied = [None, None]
+    topk_all = torch.from_numpy(np.ascontiguousarray(p.ids.transpose(1, 0, 2))).cuda()
+    torch.cuda.synchronize()
+    for t in range(w.steps):
+        b = t % 2
+        if copied[b] is not None:
+            main.wait_event(copied[b])  # the copy that read this plan buffer is done
+        hm.hs_plan(p.sw.ctx, topk_all[t], None, out, misses[b], status, plans[b], main)
+        planned = torch.cuda.Event()
+        planned.record(main)
+        side.wait_event(planned)
+        hm.hs_copy(p.sw.ctx, plans[b], misses[b], side)
+        copied[b] = torch.cuda.Event()
+        copied[b].record(side)
+        o_out, o_miss, _, _ = p.o.step(p.ids[:, t])
+        assert (out.cpu().numpy() == o_out).all() and (misses[b].cpu().numpy() == o_miss).all()
+        p.t += 1
+    torch.cuda.synchronize()
+    p.check_state()
+    p.close()
+
+
+def test_snapshot_restore_resume():
+    """A snapshot of the seven device buffers, restored, resumes exactly like the uninterrupted run."""
+    w = workload.GROW_32.with_(num_requests=4, steps=24)
+    p = Pair(w)
+    for _ in range(10):
+        p.step()
+    names = ("hot", "slot_tok", "stamp", "lru_order", "page", "step")
+    snap = {n: getattr(p.sw, n).clone() for n in names}
+    o_snap = {n: getattr(p.o, n).copy() for n in ("hot", "slot_tok", "stamp", "page", "t")}
+    first = []
+    for _ in range(10, 20):
+        p.step()
+        first.append(p.outs[0].cpu().numpy().copy())
+    for n in names:
+        getattr(p.sw, n).copy_(snap[n])
+    for n, v in o_snap.items():
+        getattr(p.o, n)[...] = v
+    p.t = 10
+    for i in range(10, 20):
+        p.step()
+        assert (p.outs[0].cpu().numpy() == first[i - 10]).all()
+    p.check_state()
+    p.close()
+
+
+def test_import_tables_and_rebuild_order():
+    """Tables computed elsewhere (here by the oracle, on the CPU) are imported without an order list;
+    hs_rebuild_order derives it from the stamps and the run continues in parity."""
+    import hierarchical_memory_amd as hm
+    w = workload.GROW_32.with_(num_requests=3, steps=20)
+    p = Pair(w)
+    ids = p.ids
+    for t in range(8):  # the oracle alone
+        p.o.step(ids[:, t])
+    for n_gpu, n_o in (("slot_tok", "slot_tok"), ("stamp", "stamp"), ("page", "page"), ("step", "t"), ("hot", "hot")):
+        getattr(p.sw, n_gpu).copy_(torch.from_numpy(np.ascontiguousarray(getattr(p.o, n_o))))
+    p.sw.lru_order.zero_()
+    hm.hs_rebuild_order(p.sw.ctx)
+    p.t = 8
+    p.check_state()
+    for _ in range(8, w.steps):
+        p.step(check_state=True)
+    p.close()
