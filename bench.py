@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="buffer-size sweep instead: B in {2048,4096,6144} x keep in {0.6,0.8,0.95}, 64 requests, "
+                         "512 steps each; reports the 100-step rolling mean of misses per step and the resolve rate")
     ap.add_argument("--split-steps", type=int, default=-1,
                     help="steps of the plan+copy leg after a reset (default: the same warmup+steps)")
     return ap.parse_args()
@@ -150,12 +153,68 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step):
             "split_step_ms": total_ms / K, "same_misses_as_fused": bool(abs(mean_m - mean_miss_per_step) < 1e-6)}
 
 
+def sweep(args) -> int:
+    """Misses per step (mean over requests, 100-step rolling mean) and resolve rate for each (B, keep) of the
+    buffer sweep; one JSON line with one entry per run."""
+    import numpy as np
+    import torch
+
+    import hierarchical_memory_amd as hm
+    import workload
+    torch.cuda.set_device(0)
+    runs = []
+    for w in workload.sweep_workloads():
+        R, k, B, H, rb = w.num_requests, w.top_k, w.buffer_slots, w.host_rows, w.row_bytes
+        sw = hm.SwapIn(hm.config(R, k, B, 0.0, rb, H, 0))
+        workload.fill_rows_ptr(sw.host_pool_address(), 0, R * H, w.row_elems, w.row_seed)
+        ids = workload.streams(w)
+        topk = torch.from_numpy(np.ascontiguousarray(ids.transpose(1, 0, 2))).cuda()
+        out = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        miss = torch.zeros((w.steps, R), dtype=torch.int32, device="cuda")
+        status = torch.zeros((w.steps, R), dtype=torch.int32, device="cuda")
+        stream = torch.cuda.current_stream()
+        W = min(args.warmup, w.steps // 4)
+        for t in range(W):
+            hm.hs_resolve(sw.ctx, topk[t], None, out, miss[t], status[t], None, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for t in range(W, w.steps):
+            hm.hs_resolve(sw.ctx, topk[t], None, out, miss[t], status[t], None, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        if status.cpu().numpy().any():
+            raise SystemExit(f"{w.name}: device status bits set")
+        m = miss.cpu().numpy().astype(np.float64).mean(axis=1)          # misses per request, per step
+        roll = np.convolve(m, np.ones(100) / 100, mode="valid")          # step 99 onwards
+        n = w.steps - W
+        timed_miss = miss[W:].cpu().numpy().astype(np.int64).sum()
+        run = {"buffer_slots": B, "keep": w.keep_permille / 1000, "steps": w.steps,
+               "miss_per_request_step_rolling100_at": {str(t): round(float(roll[t - 99]), 2)
+                                                      for t in (99, 199, 299, 399, w.steps - 1)},
+               "miss_per_request_step_mean_after_step_99": round(float(m[99:].mean()), 2),
+               "entries_per_s": n * R * k / (ms / 1e3), "ms_per_step": ms / n,
+               "miss_copy_GBps": timed_miss * rb / (ms / 1e3) / 1e9}
+        log(f"[sweep] B={B} keep={w.keep_permille / 1000}: misses/request-step {run['miss_per_request_step_mean_after_step_99']}"
+            f", {run['ms_per_step']:.3f} ms/step, {run['entries_per_s'] / 1e6:.0f} M entries/s")
+        runs.append(run)
+        sw.close()
+        del topk
+    print(json.dumps({"metric": "buffer sweep: misses per request-step (100-step rolling mean) and resolve rate",
+                      "workload": "sweep_64req_L65536_k2048", "n_gpus": 1, "data": "synthetic", "runs": runs}),
+          flush=True)
+    return 0
+
+
 def main() -> int:
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the swap-in path shards by request with no exchange between GPUs, "
               f"so --gpus {args.gpus} is not run here", file=sys.stderr)
         return 2
+    if args.sweep:
+        return sweep(args)
     import numpy as np
     import torch
 

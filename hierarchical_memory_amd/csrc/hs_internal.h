@@ -14,12 +14,11 @@ constexpr int kMaxSlots = 65535;          // slot ids fit the uint16 LRU order l
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte chunk of a row
 
 // LDS carve-up of one resolve workgroup (byte offsets; every section 16-byte aligned).
-// The hash of the selected ids is dead once hits are found, so the victim list, the
-// missed ids and the per-position gather sources reuse its bytes.
+// Two sections are reused once dead: the rank -> first position table holds the victim list from
+// phase 5 on, and the per-position ranks hold the missed ids from phase 6 on.
 struct Layout {
-  uint32_t ids, cls, pos_slot, stok, ord, sflag, bitmap, wpre, hash_key, hash_pos, vict, mtok, gsrc, misc;
-  uint32_t hash_bits;  // capacity 2^hash_bits >= 2k
-  uint32_t words;      // miss bitmap words = ceil(H / 32)
+  uint32_t ids, cls, pos_slot, rank, stok, ord, sflag, sel, selpre, first, mbits, mpre, vict, mtok, gsrc, misc;
+  uint32_t words;  // bitmap words = ceil(H / 32)
   uint32_t total;
 };
 
@@ -27,30 +26,24 @@ inline uint32_t align16(uint64_t x) { return (uint32_t)((x + 15) & ~uint64_t(15)
 
 inline Layout make_layout(int k, int B, int H) {
   Layout L{};
-  uint32_t bits = 1;
-  while ((1u << bits) < 2u * (uint32_t)k) ++bits;
-  L.hash_bits = bits;
-  const uint64_t hcap = 1ull << bits;
   L.words = (uint32_t)(((uint64_t)H + 31) / 32);
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) { uint32_t o = (uint32_t)off; off = align16(off + bytes); return o; };
   L.ids = take(4ull * k);
   L.cls = take(1ull * k);
   L.pos_slot = take(4ull * k);
+  L.rank = take(4ull * k);
   L.stok = take(4ull * B);
   L.ord = take(2ull * B);
   L.sflag = take(1ull * B);
-  L.bitmap = take(4ull * L.words);
-  L.wpre = take(2ull * L.words);  // uint16 prefix counts (k <= 8192)
-  // hash region, later reused
-  const uint64_t hash_bytes = 8ull * hcap;
-  const uint64_t lists_bytes = 3ull * align16(4ull * k);  // vict, mtok, gsrc
-  const uint32_t region = take(hash_bytes > lists_bytes ? hash_bytes : lists_bytes);
-  L.hash_key = region;
-  L.hash_pos = region + (uint32_t)(4ull * hcap);
-  L.vict = region;
-  L.mtok = region + align16(4ull * k);
-  L.gsrc = L.mtok + align16(4ull * k);
+  L.sel = take(4ull * L.words);
+  L.selpre = take(2ull * L.words);  // uint16 prefix counts (k <= 8192)
+  L.first = take(4ull * k);
+  L.mbits = take(4ull * L.words);
+  L.mpre = take(2ull * L.words);
+  L.vict = L.first;
+  L.mtok = L.rank;
+  L.gsrc = take(4ull * k);
   L.misc = take(4ull * (4 * kWaves + 8));
   L.total = (uint32_t)off;
   return L;

@@ -8,23 +8,28 @@
 // gather of "vLLM GLM 5.3 最適化: Hybrid HiSparse オフローディング", section 2
 // Mixed Residency:
 //   phase 0  coalesced loads of the selected ids, the slot->token table and the
-//            LRU order list into LDS; ids classified (padding, bad, resident,
-//            candidate); LDS scratch cleared;
-//   phase 1  candidate and resident ids inserted into an LDS hash (id -> first
-//            position), so repeats are found with set semantics;
-//   phase 2  every slot probes the hash with its token: a hit;
-//   phase 3  missed ids set bits in an LDS bitmap over token ids;
-//   phase 4  wave-segmented ballot/popcount scans: the rank of every missed id
-//            among the misses (ascending id) and of every non-hit slot in the
-//            LRU order (the first m are the victims); the new LRU order is
-//            written as the surviving candidates followed by the hit and
-//            victim slots in slot order;
-//   phase 5  j-th missed id -> j-th victim: page table, slot table and stamps;
-//   phase 6  wavefronts copy the missed rows, 16 bytes per lane, straight from
+//            LRU order list into LDS, all issued before any is consumed; ids
+//            classified (padding, bad, resident, candidate);
+//   phase 1  the selected set as an LDS bitmap over token ids;
+//   phase 2  rank of every selected id among the selected ids (popcount prefix
+//            over the bitmap words); the lowest position of each rank is kept,
+//            so a repeated id is found without any order-dependent atomic;
+//   phase 3  every slot tests its token against the bitmap: a hit, found in O(1)
+//            through the token's rank;
+//   phase 4  missed ids set bits in a second bitmap;
+//   phase 5  one block scan gives each missed id its rank among the misses
+//            (ascending id) and each non-hit slot its rank in the LRU order (the
+//            first m are the victims); the surviving candidates open the new
+//            LRU order;
+//   phase 6  j-th missed id -> j-th victim: page table, slot table, stamps,
+//            outputs; the hit and victim slots close the new LRU order in slot
+//            order;
+//   phase 7  wavefronts copy the missed rows, 16 bytes per lane, straight from
 //            mapped pinned host memory into the HBM slots (and every selected
 //            row into the gather output when fused).
-// No step of the result depends on the order of LDS atomics: the hash is used
-// only as a set with min-position, and every rank comes from a prefix count.
+// Scans run over thread-contiguous chunks: a DPP scan inside each wave, one
+// exchange of the 16 wave totals through LDS. No result depends on the order of
+// LDS atomics (they are OR and MIN only).
 //
 // The LRU order list keeps each request's slots sorted by (stamp, slot). After
 // a step, the non-victim candidates keep their stamps and relative order, and
@@ -44,37 +49,44 @@ enum : int8_t { C_PAD = 0, C_BAD = 1, C_DUP = 2, C_RES = 3, C_CAND = 4, C_HIT = 
 constexpr int kStatusBadId = 1, kStatusDupId = 2, kStatusBadState = 4;
 constexpr int kUnroll = 4;  // 16-byte loads each thread keeps in flight in the copy loops
 
-// misc words in LDS
-constexpr int kMiscTotW = 0, kMiscTotC = kWaves, kMiscTotH = 2 * kWaves, kMiscStatus = 3 * kWaves;
+// misc words in LDS: one slot array of wave totals per block scan, then the status word
+constexpr int kMiscScanSel = 0, kMiscScanRank = kWaves, kMiscScanTail = 2 * kWaves, kMiscStatus = 3 * kWaves;
 
-__device__ __forceinline__ uint32_t hash_slot(int32_t x, uint32_t bits) {
-  return ((uint32_t)x * 0x9E3779B1u) >> (32u - bits);
-}
-
-__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int n = __shfl_up(v, d, 64);
-    if (lane >= d) v += n;
-  }
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2, 4, 8 inside each row of 16
+// lanes, then the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
 }
 
-__device__ __forceinline__ int hash_find(const int32_t* hkey, int32_t x, uint32_t bits, uint32_t mask) {
-  uint32_t h = hash_slot(x, bits);
-  while (true) {
-    const int32_t kx = hkey[h];
-    if (kx == x) return (int)h;
-    if (kx == -1) return -1;
-    h = (h + 1) & mask;
+// Exclusive prefix sum of one value per thread over the workgroup. sh: kWaves ints used by this call only.
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int lane, int wave, int* total) {
+  const int inc = wave_incl_scan(v);
+  if (lane == 63) sh[wave] = inc;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w2 = 0; w2 < kWaves; ++w2) {
+    const int x = sh[w2];
+    tot += x;
+    pre += (w2 < wave) ? x : 0;
   }
+  *total = tot;
+  return pre + inc - v;
 }
+
+__device__ __forceinline__ uint32_t below(int32_t x) { return (1u << (x & 31)) - 1u; }
 
 __device__ __forceinline__ v4u load_host(const v4u* p) { return __builtin_nontemporal_load(p); }
 
 }  // namespace
 
-// kPlanOnly: stop after phase 5 and write the miss list (token, victim slot) to a.plan instead of
+// kPlanOnly: stop after phase 6 and write the miss list (token, victim slot) to a.plan instead of
 // copying rows; copy_kernel then moves the rows, possibly on another stream.
 template <bool kPlanOnly>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
@@ -82,14 +94,16 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   const Layout& L = a.L;
   int32_t* ids = (int32_t*)(smem + L.ids);
   int8_t* cls = (int8_t*)(smem + L.cls);
-  int32_t* pos_slot = (int32_t*)(smem + L.pos_slot);
+  int32_t* pos_slot = (int32_t*)(smem + L.pos_slot);  // position -> slot that holds its id (hit)
+  int32_t* rnk = (int32_t*)(smem + L.rank);           // position -> rank of its id among the selected ids
   int32_t* stok = (int32_t*)(smem + L.stok);
   uint16_t* ord = (uint16_t*)(smem + L.ord);
-  uint8_t* sflag = smem + L.sflag;  // bit 0: hit this step, bit 1: victim this step
-  uint32_t* bitmap = (uint32_t*)(smem + L.bitmap);
-  uint16_t* wpre = (uint16_t*)(smem + L.wpre);
-  int32_t* hkey = (int32_t*)(smem + L.hash_key);
-  int32_t* hpos = (int32_t*)(smem + L.hash_pos);
+  uint8_t* sflag = smem + L.sflag;  // 1: hit this step, 2: victim this step
+  uint32_t* sel = (uint32_t*)(smem + L.sel);
+  uint16_t* selpre = (uint16_t*)(smem + L.selpre);
+  int32_t* first = (int32_t*)(smem + L.first);        // rank -> lowest position holding that id
+  uint32_t* mbits = (uint32_t*)(smem + L.mbits);
+  uint16_t* mpre = (uint16_t*)(smem + L.mpre);
   int32_t* vict = (int32_t*)(smem + L.vict);
   int32_t* mtok = (int32_t*)(smem + L.mtok);
   int32_t* gsrc = (int32_t*)(smem + L.gsrc);
@@ -98,46 +112,91 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x;
   const int k = a.k, B = a.B, H = a.H, T = a.T;
-  const uint32_t hbits = L.hash_bits, hmask = (1u << hbits) - 1u;
   const int W = (int)L.words;
   const bool has_tail = a.tail0 != nullptr;
   const int32_t t0 = has_tail ? a.tail0[r] : 0;
   const int32_t t = a.step[r];
   const size_t rk = (size_t)r * k, rB = (size_t)r * B, rH = (size_t)r * H;
+  // thread-contiguous chunks of bitmap words and of slots / order positions
+  const int cw = (W + kThreads - 1) / kThreads, w0 = min(W, tid * cw), w1 = min(W, w0 + cw);
+  const int cb = (B + kThreads - 1) / kThreads, s0 = min(B, tid * cb), s1 = min(B, s0 + cb);
+  auto resident = [&](int32_t x) { return has_tail && x >= t0 && (int64_t)x - (int64_t)t0 < (int64_t)T; };
   int st = 0;
 
-  // ---- phase 0: stage and classify
+  // ---- phase 0: stage and classify. The first round of every global load of the phase is issued
+  // before any of them is consumed (one HBM round trip for the common shapes), as 16-byte vectors when the
+  // sizes allow; LDS scratch is cleared while they are in flight.
   int bad = 0;
-  for (int s = tid; s < B; s += kThreads) {
-    const int32_t y = a.slot_tok[rB + s];
-    const uint16_t o = a.order[rB + s];
-    stok[s] = y;
-    ord[s] = o;
-    sflag[s] = 0;
-    bad |= (y < -1 || y >= H || (int)o >= B);
-  }
-  for (int i = tid; i < k; i += kThreads) {
-    const int32_t x = a.topk[rk + i];
-    int8_t c;
-    if (x == -1) c = C_PAD;
-    else if (x < 0 || x >= H) { c = C_BAD; st |= kStatusBadId; }
-    else if (has_tail && x >= t0) {
-      if ((int64_t)x - (int64_t)t0 < (int64_t)T) c = C_RES;
-      else { c = C_BAD; st |= kStatusBadId; }
-    } else c = C_CAND;
-    ids[i] = x;
-    cls[i] = c;
-    pos_slot[i] = -1;
-  }
-  for (uint32_t h = tid; h <= hmask; h += kThreads) { hkey[h] = -1; hpos[h] = INT_MAX; }
-  for (int w = tid; w < W; w += kThreads) bitmap[w] = 0u;
+  const bool vecB = (B & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.slot_tok + rB) & 15) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(a.order + rB) & 7) == 0);
+  const bool veck = (k & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.topk + rk) & 15) == 0);
+  const int n4B = vecB ? (B >> 2) : 0, n4k = veck ? (k >> 2) : 0;
+  const int4* st4 = reinterpret_cast<const int4*>(a.slot_tok + rB);
+  const uint2* or4 = reinterpret_cast<const uint2*>(a.order + rB);
+  const int4* tk4 = reinterpret_cast<const int4*>(a.topk + rk);
+  int4 y0 = make_int4(-1, -1, -1, -1), x0 = make_int4(-1, -1, -1, -1);
+  uint2 o0 = make_uint2(0u, 0u);
+  if (tid < n4B) { y0 = st4[tid]; o0 = or4[tid]; }
+  if (tid < n4k) x0 = tk4[tid];
+  for (int w = tid; w < W; w += kThreads) { sel[w] = 0u; mbits[w] = 0u; }
+  for (int i = tid; i < k; i += kThreads) first[i] = INT_MAX;
   if (tid == 0) misc[kMiscStatus] = 0;
+
+  auto stage4 = [&](int i, int4 y, uint2 o) {
+    reinterpret_cast<int4*>(stok)[i] = y;
+    reinterpret_cast<uint2*>(ord)[i] = o;
+    reinterpret_cast<uint32_t*>(sflag)[i] = 0u;
+    const int yy[4] = {y.x, y.y, y.z, y.w};
+    const uint32_t oo[4] = {o.x & 0xffffu, o.x >> 16, o.y & 0xffffu, o.y >> 16};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) bad |= (yy[c] < -1 || yy[c] >= H || (int)oo[c] >= B);
+  };
+  auto classify = [&](int32_t x) -> int8_t {
+    if (x == -1) return C_PAD;
+    if (x < 0 || x >= H) { st |= kStatusBadId; return C_BAD; }
+    if (has_tail && x >= t0) {
+      if ((int64_t)x - (int64_t)t0 < (int64_t)T) return C_RES;
+      st |= kStatusBadId;
+      return C_BAD;
+    }
+    return C_CAND;
+  };
+  auto ids4 = [&](int i, int4 x) {
+    reinterpret_cast<int4*>(ids)[i] = x;
+    reinterpret_cast<int4*>(pos_slot)[i] = make_int4(-1, -1, -1, -1);
+    const uint32_t c = (uint32_t)(uint8_t)classify(x.x) | ((uint32_t)(uint8_t)classify(x.y) << 8) |
+                       ((uint32_t)(uint8_t)classify(x.z) << 16) | ((uint32_t)(uint8_t)classify(x.w) << 24);
+    reinterpret_cast<uint32_t*>(cls)[i] = c;
+  };
+
+  if (tid < n4B) stage4(tid, y0, o0);
+  for (int i = tid + kThreads; i < n4B; i += kThreads) stage4(i, st4[i], or4[i]);
+  if (!vecB) {
+    for (int s = tid; s < B; s += kThreads) {
+      const int32_t y = a.slot_tok[rB + s];
+      const uint16_t o = a.order[rB + s];
+      stok[s] = y;
+      ord[s] = o;
+      sflag[s] = 0;
+      bad |= (y < -1 || y >= H || (int)o >= B);
+    }
+  }
+  if (tid < n4k) ids4(tid, x0);
+  for (int i = tid + kThreads; i < n4k; i += kThreads) ids4(i, tk4[i]);
+  if (!veck) {
+    for (int i = tid; i < k; i += kThreads) {
+      const int32_t x = a.topk[rk + i];
+      ids[i] = x;
+      cls[i] = classify(x);
+      pos_slot[i] = -1;
+    }
+  }
   bad = __syncthreads_or(bad);
 
   if (bad) {
     // impossible state: leave the request untouched
     for (int i = tid; i < k; i += kThreads) a.out[rk + i] = -1;
-    if (a.gather) {
+    if (!kPlanOnly && a.gather) {
       v4u* gr = a.gather + rk * a.row16;
       const v4u z = {0u, 0u, 0u, 0u};
       for (int c = tid; c < k * a.row16; c += kThreads) gr[c] = z;
@@ -146,42 +205,60 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     return;
   }
 
-  // ---- phase 1: hash of candidate and resident ids (value = first position)
+  // ---- phase 1: the selected set (candidate and resident ids) as a bitmap
   for (int i = tid; i < k; i += kThreads) {
     const int8_t c = cls[i];
     if (c == C_CAND || c == C_RES) {
       const int32_t x = ids[i];
-      uint32_t h = hash_slot(x, hbits);
-      while (true) {
-        const int32_t old = atomicCAS(&hkey[h], -1, x);
-        if (old == -1 || old == x) { atomicMin(&hpos[h], i); break; }
-        h = (h + 1) & hmask;
-      }
+      atomicOr(&sel[x >> 5], 1u << (x & 31));
     }
   }
   __syncthreads();
 
-  // ---- phase 2: repeats, then the hit test: every slot probes the set with its token
+  // ---- phase 2: rank of each selected id; the lowest position of each rank wins
+  {
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
+    int n_sel;
+    int run = block_excl_scan(cnt, misc + kMiscScanSel, lane, wave, &n_sel);
+    for (int w = w0; w < w1; ++w) {
+      selpre[w] = (uint16_t)run;
+      run += __popc(sel[w]);
+    }
+  }
+  __syncthreads();
   for (int i = tid; i < k; i += kThreads) {
     const int8_t c = cls[i];
     if (c == C_CAND || c == C_RES) {
-      const int h = hash_find(hkey, ids[i], hbits, hmask);
-      if (hpos[h] != i) { cls[i] = C_DUP; st |= kStatusDupId; }
+      const int32_t x = ids[i];
+      const int q = (int)selpre[x >> 5] + __popc(sel[x >> 5] & below(x));
+      rnk[i] = q;
+      atomicMin(&first[q], i);
     }
   }
-  for (int s = tid; s < B; s += kThreads) {
+  __syncthreads();
+
+  // ---- phase 3: repeats, then the hit test: every slot looks its token up in the selected set
+  for (int i = tid; i < k; i += kThreads) {
+    const int8_t c = cls[i];
+    if ((c == C_CAND || c == C_RES) && first[rnk[i]] != i) {
+      cls[i] = C_DUP;
+      st |= kStatusDupId;
+    }
+  }
+  for (int s = s0; s < s1; ++s) {
     const int32_t y = stok[s];
-    if (y < 0) continue;
-    if (has_tail && y >= t0 && (int64_t)y - (int64_t)t0 < (int64_t)T) continue;  // resident: not a hit
-    const int h = hash_find(hkey, y, hbits, hmask);
-    if (h >= 0) {
-      pos_slot[hpos[h]] = s;
+    if (y < 0 || resident(y)) continue;  // empty, or resident (a resident id takes no slot)
+    const uint32_t word = sel[y >> 5];
+    if (word & (1u << (y & 31))) {
+      const int q = (int)selpre[y >> 5] + __popc(word & below(y));
+      pos_slot[first[q]] = s;
       sflag[s] = 1;
     }
   }
   __syncthreads();
 
-  // ---- phase 3: misses into the id bitmap
+  // ---- phase 4: misses into the second bitmap
   if (st) atomicOr(&misc[kMiscStatus], st);
   for (int i = tid; i < k; i += kThreads) {
     if (cls[i] == C_CAND) {
@@ -189,105 +266,74 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       else {
         cls[i] = C_MISS;
         const int32_t x = ids[i];
-        atomicOr(&bitmap[x >> 5], 1u << (x & 31));
+        atomicOr(&mbits[x >> 5], 1u << (x & 31));
       }
     }
   }
   __syncthreads();
 
-  // ---- phase 4: ranks. Each wave owns a contiguous segment of the bitmap words and of the LRU order.
-  const int segW = ((W + kWaves * 64 - 1) / (kWaves * 64)) * 64;
-  const int segB = ((B + kWaves * 64 - 1) / (kWaves * 64)) * 64;
-  const int w_lo = wave * segW, w_hi = min(W, w_lo + segW);
-  const int p_lo = wave * segB, p_hi = min(B, p_lo + segB);
+  // ---- phase 5: ranks of the misses (ascending id) and of the non-hit slots in LRU order, in one scan
+  // (misses in the low 16 bits: m <= k <= 8192; candidates in the high 16 bits: <= B <= 65535)
+  int m, ncand;
   {
-    int my = 0;
-    for (int base = w_lo; base < w_hi; base += 64) {
-      const int w = base + lane;
-      if (w < w_hi) my += __popc(bitmap[w]);
-    }
-    const int totW = wave_incl_scan(my, lane);
-    int totC = 0;
-    for (int base = p_lo; base < p_hi; base += 64) {
-      const int p = base + lane;
-      const bool f = p < p_hi && !(sflag[ord[p]] & 1);
-      totC += __popcll(__ballot(f));
-    }
-    if (lane == 63) misc[kMiscTotW + wave] = totW;
-    if (lane == 0) misc[kMiscTotC + wave] = totC;
-  }
-  __syncthreads();
-  int preW = 0, m = 0, preC = 0, ncand = 0;
-  for (int w2 = 0; w2 < kWaves; ++w2) {
-    const int aW = misc[kMiscTotW + w2], aC = misc[kMiscTotC + w2];
-    if (w2 < wave) { preW += aW; preC += aC; }
-    m += aW;
-    ncand += aC;
-  }
-  if (m > ncand) {
-    // more misses than free slots: only possible with a corrupt slot table
-    for (int i = tid; i < k; i += kThreads) a.out[rk + i] = -1;
-    if (a.gather) {
-      v4u* gr = a.gather + rk * a.row16;
-      const v4u z = {0u, 0u, 0u, 0u};
-      for (int c = tid; c < k * a.row16; c += kThreads) gr[c] = z;
-    }
-    if (tid == 0) { a.miss[r] = 0; a.status[r] = kStatusBadState; }
-    return;
-  }
-  {
-    int run = preW;
-    for (int base = w_lo; base < w_hi; base += 64) {
-      const int w = base + lane;
-      const int v = (w < w_hi) ? __popc(bitmap[w]) : 0;
-      const int inc = wave_incl_scan(v, lane);
-      if (w < w_hi) wpre[w] = (uint16_t)(run + inc - v);
-      run += __shfl(inc, 63, 64);
-    }
-    int runC = preC;
-    const uint64_t lt = (1ull << lane) - 1ull;
-    for (int base = p_lo; base < p_hi; base += 64) {
-      const int p = base + lane;
-      const int slot = p < p_hi ? (int)ord[p] : 0;
-      const bool f = p < p_hi && !(sflag[slot] & 1);
-      const uint64_t mask = __ballot(f);
-      const int rank = runC + __popcll(mask & lt);
-      if (f) {
-        if (rank < m) { vict[rank] = slot; sflag[slot] = 2; }
-        else a.order[rB + (rank - m)] = (uint16_t)slot;
+    int cm = 0, cc = 0;
+    for (int w = w0; w < w1; ++w) cm += __popc(mbits[w]);
+    for (int p = s0; p < s1; ++p) cc += !(sflag[ord[p]] & 1);
+    int tot;
+    const int pre = block_excl_scan(cm | (cc << 16), misc + kMiscScanRank, lane, wave, &tot);
+    m = tot & 0xffff;
+    ncand = (int)((uint32_t)tot >> 16);
+    if (m > ncand) {
+      // more misses than free slots: only possible with a corrupt slot table
+      for (int i = tid; i < k; i += kThreads) a.out[rk + i] = -1;
+      if (!kPlanOnly && a.gather) {
+        v4u* gr = a.gather + rk * a.row16;
+        const v4u z = {0u, 0u, 0u, 0u};
+        for (int c = tid; c < k * a.row16; c += kThreads) gr[c] = z;
       }
-      runC += __popcll(mask);
+      if (tid == 0) { a.miss[r] = 0; a.status[r] = kStatusBadState; }
+      return;
+    }
+    int run = pre & 0xffff;
+    for (int w = w0; w < w1; ++w) {
+      mpre[w] = (uint16_t)run;
+      run += __popc(mbits[w]);
+    }
+    int runC = (int)((uint32_t)pre >> 16);
+    for (int p = s0; p < s1; ++p) {
+      const int slot = ord[p];
+      if (sflag[slot] & 1) continue;
+      if (runC < m) {
+        vict[runC] = slot;
+        sflag[slot] = 2;
+      } else {
+        a.order[rB + (runC - m)] = (uint16_t)slot;
+      }
+      ++runC;
     }
   }
   __syncthreads();
 
-  // ---- phase 5: pair misses with victims; page table, slot table, stamps, outputs
+  // ---- phase 6: pair misses with victims: outputs and page table; the victims' new tokens go to the LDS
+  // copy of the slot table, written back below as coalesced rows
   for (int i = tid; i < k; i += kThreads) {
     const int8_t c = cls[i];
     const int32_t x = ids[i];
     int32_t o = -1, g = -1;
     if (c == C_MISS) {
       const int w = x >> 5;
-      const int j = (int)wpre[w] + __popc(bitmap[w] & ((1u << (x & 31)) - 1u));
+      const int j = (int)mpre[w] + __popc(mbits[w] & below(x));
       const int v = vict[j];
-      const int32_t y = stok[v];
+      const int32_t y = stok[v];  // each victim belongs to exactly one miss
       if (y >= 0) a.page[rH + y] = -1;
       a.page[rH + x] = v;
-      a.slot_tok[rB + v] = x;
-      a.stamp[rB + v] = t;
-      if (kPlanOnly) {
-        a.plan[rk * 2 + j] = x;
-        a.plan[rk * 2 + a.k + j] = v;
-      } else {
-        mtok[j] = x;
-      }
+      stok[v] = x;
+      mtok[j] = x;
       o = v;
       g = -2 - j;
     } else if (c == C_HIT) {
-      const int s = pos_slot[i];
-      a.stamp[rB + s] = t;
-      o = s;
-      g = s;
+      o = pos_slot[i];
+      g = o;
     } else if (c == C_RES) {
       o = B + (x - t0);
       g = o;
@@ -295,31 +341,32 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     a.out[rk + i] = o;
     gsrc[i] = g;
   }
-  // hit and victim slots close the new LRU order, in slot order
+  // hit and victim slots close the new LRU order, in slot order (the scan's barrier also publishes the
+  // LDS writes above)
   {
-    int cnt = 0;
-    for (int base = p_lo; base < p_hi; base += 64) {
-      const int s = base + lane;
-      cnt += __popcll(__ballot(s < p_hi && sflag[s] != 0));
+    int ch = 0;
+    for (int s = s0; s < s1; ++s) ch += sflag[s] != 0;
+    int tot;
+    int pos = (ncand - m) + block_excl_scan(ch, misc + kMiscScanTail, lane, wave, &tot);
+    for (int s = s0; s < s1; ++s) {
+      if (sflag[s] == 0) continue;
+      if (pos < B) a.order[rB + pos] = (uint16_t)s;  // pos < B always holds for a permutation
+      ++pos;
     }
-    if (lane == 0) misc[kMiscTotH + wave] = cnt;
   }
-  __syncthreads();
-  {
-    int run = ncand - m;
-    for (int w2 = 0; w2 < wave; ++w2) run += misc[kMiscTotH + w2];
-    const uint64_t lt = (1ull << lane) - 1ull;
-    for (int base = p_lo; base < p_hi; base += 64) {
-      const int s = base + lane;
-      const bool f = s < p_hi && sflag[s] != 0;
-      const uint64_t mask = __ballot(f);
-      const int pos = run + __popcll(mask & lt);
-      if (f && pos < B) a.order[rB + pos] = (uint16_t)s;  // pos < B always holds for a permutation
-      run += __popcll(mask);
-    }
+  // stamps of hit and victim slots, and the victims' slot-table entries: consecutive lanes write
+  // consecutive slots
+  for (int s = tid; s < B; s += kThreads) {
+    const uint8_t f = sflag[s];
+    if (f) a.stamp[rB + s] = t;
+    if (f == 2) a.slot_tok[rB + s] = stok[s];
   }
 
   if (kPlanOnly) {
+    for (int j = tid; j < m; j += kThreads) {
+      a.plan[rk * 2 + j] = mtok[j];
+      a.plan[rk * 2 + k + j] = vict[j];
+    }
     if (tid == 0) {
       a.step[r] = t + 1;
       a.miss[r] = m;
@@ -328,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     return;
   }
 
-  // ---- phase 6: rows
+  // ---- phase 7: rows (the block scan above ended with a barrier, so mtok and gsrc are visible)
   const int row16 = a.row16;
   const v4u* hostr = a.host + rH * (size_t)row16;
   v4u* hotr = a.hot + rB * (size_t)row16;

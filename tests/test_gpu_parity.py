@@ -210,11 +210,11 @@ def test_graph_replay_equals_eager():
 def test_largest_shape_that_fits_lds():
     """Near the LDS limit of one workgroup: a wide buffer and a long context."""
     import hierarchical_memory_amd as hm
-    cfg = hm.config(2, 2048, 8192, 0.0, 1152, 200000)
+    cfg = hm.config(2, 2048, 8192, 0.0, 1152, 120000)
     s = hm.hs_required_sizes(cfg)
     assert s.lds_bytes > 128 * 1024
-    w = workload.SINGLE_4K.with_(name="wide", num_requests=2, top_k=2048, buffer_slots=8192, host_rows=200000,
-                                 L0=200000, window=20000, steps=10)
+    w = workload.SINGLE_4K.with_(name="wide", num_requests=2, top_k=2048, buffer_slots=8192, host_rows=120000,
+                                 L0=120000, window=20000, steps=10)
     p = Pair(w)
     p.run(check_every=3)
     p.close()
