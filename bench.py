@@ -23,6 +23,30 @@ PCIE5_X16_GBPS = 64.0      # MI355X host link, PCIe 5.0 x16, per direction (publ
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E (published)
 
 
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("hs_kernels.hip", "hs_internal.h"):
+        with open(os.path.join(ROOT, "hierarchical_memory_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name: str, kernel: str):
+    """HBM+link bytes per launch from the committed rocprofv3 --pmc summary (FETCH_SIZE, WRITE_SIZE, each
+    scaled by what the same counter reads for a 1 GiB device copy), or None when that summary was taken on
+    other kernel sources or another workload."""
+    path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_digest") != kernel_source_digest() or rec.get("workload") != workload_name:
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k["fetch_bytes"] + k["write_bytes"]
+
+
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
@@ -39,6 +63,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="buffer-size sweep instead: B in {2048,4096,6144} x keep in {0.6,0.8,0.95}, 64 requests, "
                          "512 steps each; reports the 100-step rolling mean of misses per step and the resolve rate")
+    ap.add_argument("--trial-steps", type=int, default=256,
+                    help="steps of the hs_trial + hs_commit leg after a reset (0: skip)")
     ap.add_argument("--split-steps", type=int, default=-1,
                     help="steps of the plan+copy leg after a reset (default: the same warmup+steps)")
     return ap.parse_args()
@@ -149,6 +175,7 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step):
     return {"kernel": "resolve_kernel<plan> (hs_plan)", "bound": "hbm", "achieved": hit_gbps, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": hit_gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": meta,
             "avg_launch_us": plan_avg * 1e3, "p50_launch_us": float(np.median(plan_ms)) * 1e3,
+            "traffic": measured_traffic(w.name, "resolve_kernel<true>"),
             "copy_kernel_avg_us": float(copy_ms.mean()) * 1e3, "copy_kernel_GBps": copy_gbps,
             "split_step_ms": total_ms / K, "same_misses_as_fused": bool(abs(mean_m - mean_miss_per_step) < 1e-6)}
 
@@ -205,6 +232,46 @@ def sweep(args) -> int:
                       "workload": "sweep_64req_L65536_k2048", "n_gpus": 1, "data": "synthetic", "runs": runs}),
           flush=True)
     return 0
+
+
+def trial_leg(hm, torch, np, sw, topk, tail0, W, K, w):
+    """The same stream from a reset as hs_trial + hs_commit (every request accepted): the retryable step.
+    Its state after the leg equals the resolve leg's; the extra cost is the gather of every selected row
+    and the HBM-to-HBM move of the missed rows at commit."""
+    R, k, rb = w.num_requests, w.top_k, w.row_bytes
+    stream = torch.cuda.current_stream()
+    sw.reset()
+    trial = sw.trial_buffer()
+    out = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    miss = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
+    status = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
+    cstat = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
+    g = torch.empty((R, k, rb), dtype=torch.uint8, device="cuda")
+    for t in range(W):
+        hm.hs_trial(sw.ctx, topk[t], tail0, out, miss[t], status[t], g, trial, stream)
+        hm.hs_commit(sw.ctx, trial, g, None, cstat[t], stream)
+    torch.cuda.synchronize()
+    ea = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    eb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    for i in range(K):
+        ea[i].record(stream)
+        hm.hs_trial(sw.ctx, topk[W + i], tail0, out, miss[W + i], status[W + i], g, trial, stream)
+        eb[i].record(stream)
+        hm.hs_commit(sw.ctx, trial, g, None, cstat[W + i], stream)
+    ea[K].record(stream)
+    torch.cuda.synchronize()
+    if status[W:].cpu().numpy().any() or cstat[W:].cpu().numpy().any():
+        raise SystemExit("device status bits set during the trial leg")
+    trial_ms = np.array([ea[i].elapsed_time(eb[i]) for i in range(K)])
+    commit_ms = np.array([eb[i].elapsed_time(ea[i + 1]) for i in range(K)])
+    total = ea[0].elapsed_time(ea[K])
+    mean_m = miss[W:].cpu().numpy().astype(np.int64).sum() / K
+    del g
+    log(f"[bench] trial+commit: {total / K:.3f} ms/step (trial {trial_ms.mean() * 1e3:.0f} us, commit "
+        f"{commit_ms.mean() * 1e3:.0f} us)")
+    return {"steps": K, "warmup": W, "step_ms": total / K, "trial_avg_us": float(trial_ms.mean()) * 1e3,
+            "commit_avg_us": float(commit_ms.mean()) * 1e3,
+            "entries_per_s": K * R * k / (total / 1e3), "miss_rows_per_request_step": mean_m / R}
 
 
 def main() -> int:
@@ -313,7 +380,7 @@ def main() -> int:
         "measured_hbm_copy_GBps": hbm_copy,
         "step_ms_p10_p50_p90": [float(np.percentile(per, q)) for q in (10, 50, 90)],
         "roofline": {"bound": "host_link", "achieved": miss_gbps, "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-                     "frac": miss_gbps / PCIE5_X16_GBPS, "traffic": None,
+                     "frac": miss_gbps / PCIE5_X16_GBPS, "traffic": measured_traffic(w.name, "resolve_kernel<false>"),
                      "kernel": "resolve_kernel",
                      "algorithmic_bytes_per_launch": miss_bytes / K},
         "hbm": {"achieved": hbm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hbm_gbps / HBM_PEAK_GBPS,
@@ -322,6 +389,9 @@ def main() -> int:
     if args.split_steps != 0:
         rep["hit_path"] = split_leg(hm, torch, np, sw, topk, tail0, W, K if args.split_steps < 0 else args.split_steps,
                                     w, total_miss / K)
+    if args.trial_steps > 0:
+        kt = min(args.trial_steps, K)
+        rep["trial_commit"] = trial_leg(hm, torch, np, sw, topk, tail0, W, kt, w)
     sw.close()
     del topk
     if not args.no_cpu_baseline:

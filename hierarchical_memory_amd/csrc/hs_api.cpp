@@ -92,6 +92,7 @@ void fill_sizes(const hs_config* cfg, int32_t H, const hs::Layout& L, hs_sizes* 
   s->out_bytes = R * k * 4;
   s->gather_bytes = R * k * rb;
   s->plan_bytes = R * 2 * k * 4;
+  s->trial_bytes = R * (uint64_t)hs::trial_words((int)k, (int)B) * 4;
   s->lds_bytes = L.total;
 }
 
@@ -237,7 +238,7 @@ int hs_reset(hs_ctx* ctx, const int32_t* d_request_ids, int32_t n, void* stream)
 namespace {
 
 int resolve_common(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
-                   int32_t* d_status, void* d_gather, int32_t* d_plan, void* stream) {
+                   int32_t* d_status, void* d_gather, int32_t* d_plan, int32_t* d_trial, void* stream) {
   int rc = check_ready(ctx);
   if (rc) return rc;
   if (!d_topk || !d_out || !d_miss || !d_status)
@@ -268,8 +269,11 @@ int resolve_common(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, i
   a.status = d_status;
   a.gather = (hs::v4u*)d_gather;
   a.plan = d_plan;
+  a.trial = d_trial;
+  a.trial_words = hs::trial_words(a.k, a.B);
+  if (d_trial && !aligned(d_trial, 16)) return fail(HS_E_INVALID, "trial buffer is not 16-byte aligned");
   hipError_t e = hs::launch_resolve(a, (hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, d_plan ? "plan launch" : "resolve launch");
+  if (e != hipSuccess) return hip_fail(e, d_trial ? "trial launch" : d_plan ? "plan launch" : "resolve launch");
   return ok();
 }
 
@@ -279,13 +283,48 @@ extern "C" {
 
 int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
                int32_t* d_status, void* d_gather, void* stream) {
-  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, d_gather, nullptr, stream);
+  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, d_gather, nullptr, nullptr, stream);
 }
 
 int hs_plan(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
             int32_t* d_status, int32_t* d_plan, void* stream) {
   if (!d_plan) return fail(HS_E_INVALID, "plan buffer must not be NULL");
-  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, nullptr, d_plan, stream);
+  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, nullptr, d_plan, nullptr, stream);
+}
+
+int hs_trial(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
+             int32_t* d_status, void* d_gather, int32_t* d_trial, void* stream) {
+  if (!d_trial || !d_gather) return fail(HS_E_INVALID, "trial and gather buffers must not be NULL");
+  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, d_gather, nullptr, d_trial, stream);
+}
+
+int hs_commit(hs_ctx* ctx, const int32_t* d_trial, const void* d_gather, const int32_t* d_accept, int32_t* d_status,
+              void* stream) {
+  int rc = check_ready(ctx);
+  if (rc) return rc;
+  if (!d_trial || !d_gather) return fail(HS_E_INVALID, "trial and gather buffers must not be NULL");
+  if (!aligned(d_gather, 16) || !aligned(d_trial, 16))
+    return fail(HS_E_INVALID, "trial and gather buffers must be 16-byte aligned");
+  hs::CommitArgs a{};
+  a.R = ctx->cfg.num_requests;
+  a.k = ctx->cfg.top_k;
+  a.B = ctx->cfg.device_buffer_size;
+  a.H = ctx->H;
+  a.row16 = ctx->cfg.row_bytes / 16;
+  a.trial_words = hs::trial_words(a.k, a.B);
+  a.trial = d_trial;
+  a.accept = d_accept;
+  a.gather = (const hs::v4u*)d_gather;
+  a.status = d_status;
+  a.hot = (hs::v4u*)ctx->views.hot;
+  a.slot_tok = ctx->views.slot_tok;
+  a.stamp = ctx->views.stamp;
+  a.order = ctx->views.lru_order;
+  a.page = ctx->views.page;
+  a.step = ctx->views.step;
+  hipError_t e = hs::launch_commit(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "commit launch");
+  return ok();
 }
 
 int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* stream) {

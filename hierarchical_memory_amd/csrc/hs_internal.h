@@ -14,10 +14,12 @@ constexpr int kMaxSlots = 65535;          // slot ids fit the uint16 LRU order l
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte chunk of a row
 
 // LDS carve-up of one resolve workgroup (byte offsets; every section 16-byte aligned).
-// Two sections are reused once dead: the rank -> first position table holds the victim list from
-// phase 5 on, and the per-position ranks hold the missed ids from phase 6 on.
+// Sections reused once dead: the rank -> first position table holds the victim list from phase 4 on,
+// the per-position ranks hold the missed ids from phase 5 on, and the prefix counts of the selected set
+// become the prefix counts of the misses.
 struct Layout {
-  uint32_t ids, cls, pos_slot, rank, stok, ord, sflag, sel, selpre, first, mbits, mpre, vict, mtok, gsrc, misc;
+  uint32_t ids, cls, pos_slot, rank, stok, ord, sflag, sel, cbits, hbits, selpre, first, mpre, vict, mtok, gsrc,
+      misc;
   uint32_t words;  // bitmap words = ceil(H / 32)
   uint32_t total;
 };
@@ -36,11 +38,12 @@ inline Layout make_layout(int k, int B, int H) {
   L.stok = take(4ull * B);
   L.ord = take(2ull * B);
   L.sflag = take(1ull * B);
-  L.sel = take(4ull * L.words);
-  L.selpre = take(2ull * L.words);  // uint16 prefix counts (k <= 8192)
+  L.sel = take(4ull * L.words);    // selected ids (candidates and resident)
+  L.cbits = take(4ull * L.words);  // candidate ids (not resident)
+  L.hbits = take(4ull * L.words);  // candidate ids found in a slot
+  L.selpre = take(2ull * L.words); // uint16 prefix counts (k <= 8192)
   L.first = take(4ull * k);
-  L.mbits = take(4ull * L.words);
-  L.mpre = take(2ull * L.words);
+  L.mpre = L.selpre;
   L.vict = L.first;
   L.mtok = L.rank;
   L.gsrc = take(4ull * k);
@@ -67,6 +70,27 @@ struct ResolveArgs {
   int32_t* status;
   v4u* gather;
   int32_t* plan;    // non-null: plan-only launch, [R][2][k] (missed tokens, then their victim slots)
+  int32_t* trial;   // non-null: trial launch, [R][trial_words]
+  int64_t trial_words;
+};
+
+// Words of one request's trial record: 4 header words, 4 lists of k, the new order as B uint16, rounded
+// up to 16 bytes.
+inline int64_t trial_words(int k, int B) { return ((4 + 4ll * k + (B + 1) / 2) + 3) & ~3ll; }
+
+struct CommitArgs {
+  int32_t R, k, B, H, row16;
+  int64_t trial_words;
+  const int32_t* trial;
+  const int32_t* accept;  // [R] or nullptr (all)
+  const v4u* gather;      // [R][k][row16]
+  int32_t* status;        // [R] or nullptr
+  v4u* hot;
+  int32_t* slot_tok;
+  int32_t* stamp;
+  uint16_t* order;
+  int32_t* page;
+  int32_t* step;
 };
 
 struct CopyArgs {
@@ -106,6 +130,7 @@ hipError_t launch_reset(const ResetArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_rebuild_order(const RebuildArgs& a, hipStream_t s);
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes);
 
 }  // namespace hs

@@ -10,21 +10,22 @@
 //   phase 0  coalesced loads of the selected ids, the slot->token table and the
 //            LRU order list into LDS, all issued before any is consumed; ids
 //            classified (padding, bad, resident, candidate);
-//   phase 1  the selected set as an LDS bitmap over token ids;
+//   phase 1  the selected set, and the candidates among it (not resident), as
+//            LDS bitmaps over token ids;
 //   phase 2  rank of every selected id among the selected ids (popcount prefix
 //            over the bitmap words); the lowest position of each rank is kept,
 //            so a repeated id is found without any order-dependent atomic;
 //   phase 3  every slot tests its token against the bitmap: a hit, found in O(1)
-//            through the token's rank;
-//   phase 4  missed ids set bits in a second bitmap;
-//   phase 5  one block scan gives each missed id its rank among the misses
+//            through the token's rank, also marked in a hit bitmap, so the
+//            missed ids are the candidate bits without a hit bit;
+//   phase 4  one block scan gives each missed id its rank among the misses
 //            (ascending id) and each non-hit slot its rank in the LRU order (the
 //            first m are the victims); the surviving candidates open the new
 //            LRU order;
-//   phase 6  j-th missed id -> j-th victim: page table, slot table, stamps,
+//   phase 5  j-th missed id -> j-th victim: page table, slot table, stamps,
 //            outputs; the hit and victim slots close the new LRU order in slot
 //            order;
-//   phase 7  wavefronts copy the missed rows, 16 bytes per lane, straight from
+//   phase 6  wavefronts copy the missed rows, 16 bytes per lane, straight from
 //            mapped pinned host memory into the HBM slots (and every selected
 //            row into the gather output when fused).
 // Scans run over thread-contiguous chunks: a DPP scan inside each wave, one
@@ -44,9 +45,9 @@ namespace hs {
 
 namespace {
 
-enum : int8_t { C_PAD = 0, C_BAD = 1, C_DUP = 2, C_RES = 3, C_CAND = 4, C_HIT = 5, C_MISS = 6 };
+enum : int8_t { C_PAD = 0, C_BAD = 1, C_DUP = 2, C_RES = 3, C_CAND = 4 };
 
-constexpr int kStatusBadId = 1, kStatusDupId = 2, kStatusBadState = 4;
+constexpr int kStatusBadId = 1, kStatusDupId = 2, kStatusBadState = 4, kStatusStale = 8;
 constexpr int kUnroll = 4;  // 16-byte loads each thread keeps in flight in the copy loops
 
 // misc words in LDS: one slot array of wave totals per block scan, then the status word
@@ -84,11 +85,32 @@ __device__ __forceinline__ uint32_t below(int32_t x) { return (1u << (x & 31)) -
 
 __device__ __forceinline__ v4u load_host(const v4u* p) { return __builtin_nontemporal_load(p); }
 
+constexpr int kFused = 0, kPlan = 1, kTrial = 2;
+constexpr int kTrialHead = 4;
+
+// Trial record of one request (int32 words): [m, first tail position of the new order, step, 0], then
+// k missed tokens, k victim slots, k evicted tokens (-1: slot was empty), k positions in the selection,
+// then the new LRU order as B uint16.
+__device__ __forceinline__ int32_t* trial_rec(const ResolveArgs& a, int r) { return a.trial + (size_t)r * a.trial_words; }
+
+__device__ __forceinline__ void trial_header(const ResolveArgs& a, int r, int m, int tail_start, int step) {
+  int32_t* rec = trial_rec(a, r);
+  rec[0] = m;
+  rec[1] = tail_start;
+  rec[2] = step;
+  rec[3] = 0;
+}
+
 }  // namespace
 
-// kPlanOnly: stop after phase 6 and write the miss list (token, victim slot) to a.plan instead of
-// copying rows; copy_kernel then moves the rows, possibly on another stream.
-template <bool kPlanOnly>
+// kMode selects what a launch does with the step it has ranked:
+//   kFused: commit the step and copy the rows (hs_resolve);
+//   kPlan:  commit the step and write the miss list (token, victim slot) to a.plan instead of copying
+//           rows; copy_kernel then moves the rows, possibly on another stream (hs_plan);
+//   kTrial: commit nothing; write a trial record (the new LRU order and, per miss, token, victim slot,
+//           evicted token and position) and gather every selected row, the missed ones straight from the
+//           host pool; commit_kernel applies accepted records later (hs_trial / hs_commit).
+template <int kMode>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Layout& L = a.L;
@@ -100,9 +122,10 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   uint16_t* ord = (uint16_t*)(smem + L.ord);
   uint8_t* sflag = smem + L.sflag;  // 1: hit this step, 2: victim this step
   uint32_t* sel = (uint32_t*)(smem + L.sel);
+  uint32_t* cbits = (uint32_t*)(smem + L.cbits);
+  uint32_t* hbits = (uint32_t*)(smem + L.hbits);
   uint16_t* selpre = (uint16_t*)(smem + L.selpre);
   int32_t* first = (int32_t*)(smem + L.first);        // rank -> lowest position holding that id
-  uint32_t* mbits = (uint32_t*)(smem + L.mbits);
   uint16_t* mpre = (uint16_t*)(smem + L.mpre);
   int32_t* vict = (int32_t*)(smem + L.vict);
   int32_t* mtok = (int32_t*)(smem + L.mtok);
@@ -111,6 +134,10 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = blockIdx.x;
+  // where the new LRU order goes: the request's order list, or the trial record
+  uint16_t* new_order = kMode == kTrial
+                            ? reinterpret_cast<uint16_t*>(a.trial + (size_t)r * a.trial_words + kTrialHead + 4 * a.k)
+                            : a.order + (size_t)r * a.B;
   const int k = a.k, B = a.B, H = a.H, T = a.T;
   const int W = (int)L.words;
   const bool has_tail = a.tail0 != nullptr;
@@ -138,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   uint2 o0 = make_uint2(0u, 0u);
   if (tid < n4B) { y0 = st4[tid]; o0 = or4[tid]; }
   if (tid < n4k) x0 = tk4[tid];
-  for (int w = tid; w < W; w += kThreads) { sel[w] = 0u; mbits[w] = 0u; }
+  for (int w = tid; w < W; w += kThreads) { sel[w] = 0u; cbits[w] = 0u; hbits[w] = 0u; }
   for (int i = tid; i < k; i += kThreads) first[i] = INT_MAX;
   if (tid == 0) misc[kMiscStatus] = 0;
 
@@ -196,21 +223,23 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   if (bad) {
     // impossible state: leave the request untouched
     for (int i = tid; i < k; i += kThreads) a.out[rk + i] = -1;
-    if (!kPlanOnly && a.gather) {
+    if (kMode != kPlan && a.gather) {
       v4u* gr = a.gather + rk * a.row16;
       const v4u z = {0u, 0u, 0u, 0u};
       for (int c = tid; c < k * a.row16; c += kThreads) gr[c] = z;
     }
     if (tid == 0) { a.miss[r] = 0; a.status[r] = kStatusBadState; }
+    if (kMode == kTrial && tid == 0) trial_header(a, r, 0, 0, -1);
     return;
   }
 
-  // ---- phase 1: the selected set (candidate and resident ids) as a bitmap
+  // ---- phase 1: the selected set (candidate and resident ids) and the candidates as bitmaps
   for (int i = tid; i < k; i += kThreads) {
     const int8_t c = cls[i];
     if (c == C_CAND || c == C_RES) {
       const int32_t x = ids[i];
       atomicOr(&sel[x >> 5], 1u << (x & 31));
+      if (c == C_CAND) atomicOr(&cbits[x >> 5], 1u << (x & 31));
     }
   }
   __syncthreads();
@@ -254,30 +283,18 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       const int q = (int)selpre[y >> 5] + __popc(word & below(y));
       pos_slot[first[q]] = s;
       sflag[s] = 1;
+      atomicOr(&hbits[y >> 5], 1u << (y & 31));
     }
   }
-  __syncthreads();
-
-  // ---- phase 4: misses into the second bitmap
   if (st) atomicOr(&misc[kMiscStatus], st);
-  for (int i = tid; i < k; i += kThreads) {
-    if (cls[i] == C_CAND) {
-      if (pos_slot[i] >= 0) cls[i] = C_HIT;
-      else {
-        cls[i] = C_MISS;
-        const int32_t x = ids[i];
-        atomicOr(&mbits[x >> 5], 1u << (x & 31));
-      }
-    }
-  }
   __syncthreads();
 
-  // ---- phase 5: ranks of the misses (ascending id) and of the non-hit slots in LRU order, in one scan
+  // ---- phase 4: ranks of the misses (ascending id) and of the non-hit slots in LRU order, in one scan
   // (misses in the low 16 bits: m <= k <= 8192; candidates in the high 16 bits: <= B <= 65535)
   int m, ncand;
   {
     int cm = 0, cc = 0;
-    for (int w = w0; w < w1; ++w) cm += __popc(mbits[w]);
+    for (int w = w0; w < w1; ++w) cm += __popc(cbits[w] & ~hbits[w]);
     for (int p = s0; p < s1; ++p) cc += !(sflag[ord[p]] & 1);
     int tot;
     const int pre = block_excl_scan(cm | (cc << 16), misc + kMiscScanRank, lane, wave, &tot);
@@ -286,18 +303,19 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     if (m > ncand) {
       // more misses than free slots: only possible with a corrupt slot table
       for (int i = tid; i < k; i += kThreads) a.out[rk + i] = -1;
-      if (!kPlanOnly && a.gather) {
+      if (kMode != kPlan && a.gather) {
         v4u* gr = a.gather + rk * a.row16;
         const v4u z = {0u, 0u, 0u, 0u};
         for (int c = tid; c < k * a.row16; c += kThreads) gr[c] = z;
       }
       if (tid == 0) { a.miss[r] = 0; a.status[r] = kStatusBadState; }
+      if (kMode == kTrial && tid == 0) trial_header(a, r, 0, 0, -1);
       return;
     }
     int run = pre & 0xffff;
     for (int w = w0; w < w1; ++w) {
       mpre[w] = (uint16_t)run;
-      run += __popc(mbits[w]);
+      run += __popc(cbits[w] & ~hbits[w]);
     }
     int runC = (int)((uint32_t)pre >> 16);
     for (int p = s0; p < s1; ++p) {
@@ -307,31 +325,40 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
         vict[runC] = slot;
         sflag[slot] = 2;
       } else {
-        a.order[rB + (runC - m)] = (uint16_t)slot;
+        new_order[runC - m] = (uint16_t)slot;
       }
       ++runC;
     }
   }
   __syncthreads();
 
-  // ---- phase 6: pair misses with victims: outputs and page table; the victims' new tokens go to the LDS
+  // ---- phase 5: pair misses with victims: outputs and page table; the victims' new tokens go to the LDS
   // copy of the slot table, written back below as coalesced rows
   for (int i = tid; i < k; i += kThreads) {
     const int8_t c = cls[i];
     const int32_t x = ids[i];
     int32_t o = -1, g = -1;
-    if (c == C_MISS) {
+    const bool cand = c == C_CAND;
+    if (cand && pos_slot[i] < 0) {  // a miss
       const int w = x >> 5;
-      const int j = (int)mpre[w] + __popc(mbits[w] & below(x));
+      const int j = (int)mpre[w] + __popc(cbits[w] & ~hbits[w] & below(x));
       const int v = vict[j];
       const int32_t y = stok[v];  // each victim belongs to exactly one miss
-      if (y >= 0) a.page[rH + y] = -1;
-      a.page[rH + x] = v;
+      if (kMode == kTrial) {
+        int32_t* rec = trial_rec(a, r);
+        rec[kTrialHead + j] = x;
+        rec[kTrialHead + k + j] = v;
+        rec[kTrialHead + 2 * k + j] = y;
+        rec[kTrialHead + 3 * k + j] = i;
+      } else {
+        if (y >= 0) a.page[rH + y] = -1;
+        a.page[rH + x] = v;
+      }
       stok[v] = x;
       mtok[j] = x;
       o = v;
       g = -2 - j;
-    } else if (c == C_HIT) {
+    } else if (cand) {  // a hit
       o = pos_slot[i];
       g = o;
     } else if (c == C_RES) {
@@ -350,19 +377,21 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     int pos = (ncand - m) + block_excl_scan(ch, misc + kMiscScanTail, lane, wave, &tot);
     for (int s = s0; s < s1; ++s) {
       if (sflag[s] == 0) continue;
-      if (pos < B) a.order[rB + pos] = (uint16_t)s;  // pos < B always holds for a permutation
+      if (pos < B) new_order[pos] = (uint16_t)s;  // pos < B always holds for a permutation
       ++pos;
     }
   }
   // stamps of hit and victim slots, and the victims' slot-table entries: consecutive lanes write
   // consecutive slots
-  for (int s = tid; s < B; s += kThreads) {
-    const uint8_t f = sflag[s];
-    if (f) a.stamp[rB + s] = t;
-    if (f == 2) a.slot_tok[rB + s] = stok[s];
+  if (kMode != kTrial) {
+    for (int s = tid; s < B; s += kThreads) {
+      const uint8_t f = sflag[s];
+      if (f) a.stamp[rB + s] = t;
+      if (f == 2) a.slot_tok[rB + s] = stok[s];
+    }
   }
 
-  if (kPlanOnly) {
+  if (kMode == kPlan) {
     for (int j = tid; j < m; j += kThreads) {
       a.plan[rk * 2 + j] = mtok[j];
       a.plan[rk * 2 + k + j] = vict[j];
@@ -375,7 +404,9 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     return;
   }
 
-  // ---- phase 7: rows (the block scan above ended with a barrier, so mtok and gsrc are visible)
+  if (kMode == kTrial && tid == 0) trial_header(a, r, m, ncand - m, t);
+
+  // ---- phase 6: rows (the block scan above ended with a barrier, so mtok and gsrc are visible)
   const int row16 = a.row16;
   const v4u* hostr = a.host + rH * (size_t)row16;
   v4u* hotr = a.hot + rB * (size_t)row16;
@@ -417,7 +448,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
           if (g <= -2) {
             const int j = -2 - g;
             v[u] = load_host(hostr + (size_t)mtok[j] * row16 + q);
-            hot_dst[u] = (long long)vict[j] * row16 + q;
+            if (kMode != kTrial) hot_dst[u] = (long long)vict[j] * row16 + q;
           } else if (g >= B) {
             v[u] = tailr[(size_t)(g - B) * row16 + q];
           } else if (g >= 0) {
@@ -437,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   }
 
   if (tid == 0) {
-    a.step[r] = t + 1;
+    if (kMode != kTrial) a.step[r] = t + 1;
     a.miss[r] = m;
     a.status[r] = misc[kMiscStatus];
   }
@@ -507,6 +538,67 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
   }
 }
 
+// Applies accepted trial records: the new LRU order, stamp t for the hit and victim slots (the new order's
+// tail), the victims' slot-table and page-table entries, the step counter, and each missed row copied from
+// the gather output (where the trial put it) into its victim slot. A record whose step no longer matches
+// the request's step counter is stale and is not applied.
+__global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint8_t* used = smem;  // B flags: slot in the new order's tail
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (a.accept && a.accept[r] == 0) {
+    if (a.status && tid == 0) a.status[r] = 0;
+    return;
+  }
+  const int k = a.k, B = a.B, H = a.H;
+  const int32_t* rec = a.trial + (size_t)r * a.trial_words;
+  const int m = rec[0], u0 = rec[1], t = rec[2];
+  if (t < 0 || a.step[r] != t || m < 0 || m > k || u0 < 0 || u0 > B) {
+    if (a.status && tid == 0) a.status[r] = kStatusStale;
+    return;
+  }
+  const size_t rB = (size_t)r * B, rH = (size_t)r * H, rk = (size_t)r * k;
+  const uint16_t* nord = reinterpret_cast<const uint16_t*>(rec + kTrialHead + 4 * k);
+  for (int s = tid; s < B; s += blockDim.x) used[s] = 0;
+  __syncthreads();
+  for (int p = tid; p < B; p += blockDim.x) {
+    const int o = nord[p];
+    if (o >= B) continue;  // only a corrupt record
+    a.order[rB + p] = (uint16_t)o;
+    if (p >= u0) used[o] = 1;
+  }
+  __syncthreads();
+  for (int s = tid; s < B; s += blockDim.x)
+    if (used[s]) a.stamp[rB + s] = t;
+  const int32_t* tok = rec + kTrialHead;
+  const int32_t* slot = tok + k;
+  const int32_t* evicted = slot + k;
+  const int32_t* pos = evicted + k;
+  for (int j = tid; j < m; j += blockDim.x) {
+    const int x = tok[j], v = slot[j], y = evicted[j];
+    if (x < 0 || x >= H || v < 0 || v >= B) continue;
+    if (y >= 0 && y < H) a.page[rH + y] = -1;
+    a.page[rH + x] = v;
+    a.slot_tok[rB + v] = x;
+  }
+  const int row16 = a.row16, total = m * row16;
+  for (int c = tid; c < total; c += blockDim.x) {
+    const int j = c / row16, q = c - j * row16;
+    const int v = slot[j], i = pos[j];
+    if (v < 0 || v >= B || i < 0 || i >= k) continue;
+    a.hot[(rB + v) * row16 + q] = a.gather[(rk + i) * row16 + q];
+  }
+  if (tid == 0) {
+    a.step[r] = t + 1;
+    if (a.status) a.status[r] = 0;
+  }
+}
+
+hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(commit_kernel, dim3(a.R), dim3(1024), (size_t)a.B, s, a);
+  return hipGetLastError();
+}
+
 // Rebuilds request r's LRU order list from its stamps: the rank of slot s is the number of slots with a
 // smaller (stamp, slot) key, counted against all B stamps staged in LDS. Used after a caller imports
 // tables that did not carry the order list; O(B^2 / 1024) per thread, off the decode path.
@@ -534,19 +626,25 @@ hipError_t launch_rebuild_order(const RebuildArgs& a, hipStream_t s) {
 }
 
 hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes) {
-  hipError_t e = hipFuncSetAttribute((const void*)resolve_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  hipError_t e = hipFuncSetAttribute((const void*)resolve_kernel<kFused>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)resolve_bytes);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)resolve_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  e = hipFuncSetAttribute((const void*)resolve_kernel<kPlan>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)resolve_bytes);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)resolve_kernel<kTrial>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)resolve_bytes);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)commit_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rebuild_bytes);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute((const void*)rebuild_order_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                              (int)rebuild_bytes);
 }
 
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {
-  if (a.plan) hipLaunchKernelGGL(resolve_kernel<true>, dim3(a.R), dim3(kThreads), a.L.total, s, a);
-  else hipLaunchKernelGGL(resolve_kernel<false>, dim3(a.R), dim3(kThreads), a.L.total, s, a);
+  if (a.trial) hipLaunchKernelGGL(resolve_kernel<kTrial>, dim3(a.R), dim3(kThreads), a.L.total, s, a);
+  else if (a.plan) hipLaunchKernelGGL(resolve_kernel<kPlan>, dim3(a.R), dim3(kThreads), a.L.total, s, a);
+  else hipLaunchKernelGGL(resolve_kernel<kFused>, dim3(a.R), dim3(kThreads), a.L.total, s, a);
   return hipGetLastError();
 }
 

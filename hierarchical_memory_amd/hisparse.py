@@ -17,10 +17,11 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhispars
 _lib = None
 
 HS_OK, HS_E_INVALID, HS_E_NOMEM, HS_E_HIP, HS_E_STATE = 0, -1, -2, -3, -4
-HS_STATUS_BAD_ID, HS_STATUS_DUP_ID, HS_STATUS_BAD_STATE = 1, 2, 4
+HS_STATUS_BAD_ID, HS_STATUS_DUP_ID, HS_STATUS_BAD_STATE, HS_STATUS_STALE = 1, 2, 4, 8
 
 EXPORTED = ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
-            "hs_plan", "hs_copy", "hs_gather", "hs_rebuild_order", "hs_destroy", "hs_last_error")
+            "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_gather", "hs_rebuild_order", "hs_destroy",
+            "hs_last_error")
 
 
 class HiSparseError(RuntimeError):
@@ -45,7 +46,7 @@ class HsSizes(ctypes.Structure):
                 ("tail_bytes", ctypes.c_uint64), ("slot_tok_bytes", ctypes.c_uint64), ("stamp_bytes", ctypes.c_uint64),
                 ("lru_order_bytes", ctypes.c_uint64), ("page_bytes", ctypes.c_uint64), ("step_bytes", ctypes.c_uint64),
                 ("topk_bytes", ctypes.c_uint64), ("out_bytes", ctypes.c_uint64), ("gather_bytes", ctypes.c_uint64),
-                ("plan_bytes", ctypes.c_uint64), ("lds_bytes", ctypes.c_uint32)]
+                ("plan_bytes", ctypes.c_uint64), ("trial_bytes", ctypes.c_uint64), ("lds_bytes", ctypes.c_uint32)]
 
 
 def library_path() -> str:
@@ -72,6 +73,8 @@ def lib():
         L.hs_resolve.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         L.hs_plan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         L.hs_copy.argtypes = [vp, vp, vp, vp]
+        L.hs_trial.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.hs_commit.argtypes = [vp, vp, vp, vp, vp, vp]
         L.hs_gather.argtypes = [vp, vp, vp, vp]
         L.hs_rebuild_order.argtypes = [vp, vp]
         L.hs_destroy.argtypes = [vp]
@@ -79,7 +82,7 @@ def lib():
         L.hs_last_error.argtypes = []
         L.hs_last_error.restype = ctypes.c_char_p
         for name in ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
-                     "hs_plan", "hs_copy", "hs_gather", "hs_rebuild_order"):
+                     "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_gather", "hs_rebuild_order"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -174,6 +177,15 @@ def hs_copy(ctx, plan, miss, stream=None) -> None:
     _check(lib().hs_copy(ctx, _ptr(plan), _ptr(miss), _stream(stream)))
 
 
+def hs_trial(ctx, topk, tail0, out, miss, status, gather, trial, stream=None) -> None:
+    _check(lib().hs_trial(ctx, _ptr(topk), _ptr(tail0), _ptr(out), _ptr(miss), _ptr(status), _ptr(gather),
+                          _ptr(trial), _stream(stream)))
+
+
+def hs_commit(ctx, trial, gather, accept=None, status=None, stream=None) -> None:
+    _check(lib().hs_commit(ctx, _ptr(trial), _ptr(gather), _ptr(accept), _ptr(status), _stream(stream)))
+
+
 def hs_gather(ctx, out, gather, stream=None) -> None:
     _check(lib().hs_gather(ctx, _ptr(out), _ptr(gather), _stream(stream)))
 
@@ -235,6 +247,10 @@ class SwapIn:
         out, miss, status, g = outputs if outputs is not None else self.outputs(gather)
         hs_resolve(self.ctx, topk, tail0, out, miss, status, g, stream)
         return out, miss, status, g
+
+    def trial_buffer(self):
+        import torch
+        return torch.empty((self.sizes.trial_bytes // 4,), dtype=torch.int32, device=self.device)
 
     def plan_buffer(self):
         import torch

@@ -58,6 +58,8 @@ extern "C" {
 #define HS_STATUS_DUP_ID 2    /* an id repeated within the request's selection (first occurrence wins) */
 #define HS_STATUS_BAD_STATE 4 /* the request's slot table or LRU order held an impossible value: nothing
                                  was changed for this request and every output is -1 */
+#define HS_STATUS_STALE 8     /* hs_commit: the trial was planned at another step than the request's current
+                                 one; it was not applied */
 
 /*
  * Configuration. top_k, device_buffer_size and host_to_device_ratio are the
@@ -100,6 +102,7 @@ typedef struct hs_sizes {
   uint64_t out_bytes;        /* [R][k] int32 output of one step */
   uint64_t gather_bytes;     /* [R][k][row_bytes] gather output */
   uint64_t plan_bytes;       /* [R][2][k] int32 miss list of hs_plan */
+  uint64_t trial_bytes;      /* trial records of hs_trial / hs_commit */
   uint32_t lds_bytes;        /* LDS one resolve workgroup uses */
 } hs_sizes;
 
@@ -155,6 +158,26 @@ int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32
 int hs_plan(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
             int32_t* d_status, int32_t* d_plan, void* stream);
 int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* stream);
+
+/*
+ * A retryable step, for speculative decoding: the vLLM page names a per-step resolver plan that can be
+ * retried and shares the request's hot state ("vLLM GLM 5.3 最適化: Hybrid HiSparse オフローディング",
+ * section vLLM エコシステムとの統合).
+ * hs_trial resolves a step exactly as hs_resolve would (same d_out, d_miss, d_status) but changes no state
+ * at all: no table, stamp, step counter or hot row. Every selected row goes to d_gather
+ * [R][k][row_bytes] (required), missed rows straight from the host pool, so the step can be verified
+ * from d_gather. d_trial (hs_sizes.trial_bytes, 16-byte aligned) receives one record per request.
+ * hs_commit applies the records of the requests with d_accept[r] != 0 (all when d_accept is NULL): LRU
+ * order, stamps, slot and page tables, step counter, and the missed rows copied from d_gather into their
+ * victim slots (HBM to HBM). Requests not accepted keep their state, so a trial is rolled back by not
+ * committing it and retried by calling hs_trial again. A record planned at another step than the
+ * request's current one is not applied and sets HS_STATUS_STALE in d_status[r] (optional, [R]). d_gather
+ * must still hold what hs_trial wrote.
+ */
+int hs_trial(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
+             int32_t* d_status, void* d_gather, int32_t* d_trial, void* stream);
+int hs_commit(hs_ctx* ctx, const int32_t* d_trial, const void* d_gather, const int32_t* d_accept, int32_t* d_status,
+              void* stream);
 
 /* Unfused gather: d_gather[r][i] = the row d_out[r][i] names (as in hs_resolve), zeros for -1 or for
  * an index outside [0, B + T). d_out [R][k] int32, d_gather [R][k][row_bytes]. */

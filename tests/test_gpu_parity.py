@@ -328,3 +328,78 @@ def test_import_tables_and_rebuild_order():
     for _ in range(8, w.steps):
         p.step(check_state=True)
     p.close()
+
+
+def _oracle_copy(o):
+    import copy
+    c = copy.copy(o)
+    for n in ("slot_tok", "stamp", "page", "t", "hot"):
+        setattr(c, n, getattr(o, n).copy())
+    return c
+
+
+def test_trial_commit_retry_matches_oracle():
+    """hs_trial changes nothing; its outputs and gathered rows equal the oracle's on a copy of the state.
+    hs_commit applies the accepted requests only; a record committed twice is stale the second time."""
+    import hierarchical_memory_amd as hm
+    w = workload.GROW_32.with_(num_requests=6, steps=14)
+    p = Pair(w, gather=True)
+    R = w.num_requests
+    trial = p.sw.trial_buffer()
+    out, miss, status, g = p.outs
+    cstat = torch.zeros((R,), dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(11)
+    names = ("slot_tok", "stamp", "lru_order", "page", "step", "hot")
+    for t in range(w.steps):
+        ids = p.ids[:, t]
+        # a first try with another selection (the next request's ids), rejected
+        alt = np.ascontiguousarray(np.roll(ids, 1, axis=0))
+        before = {n: getattr(p.sw, n).clone() for n in names}
+        hm.hs_trial(p.sw.ctx, torch.from_numpy(alt).cuda(), None, out, miss, status, g, trial)
+        oc = _oracle_copy(p.o)
+        o_out, o_miss, o_st, o_g = oc.step(alt, gather=True)
+        assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+        assert (status.cpu().numpy() == o_st).all() and (g.cpu().numpy() == o_g).all()
+        for n in names:
+            assert torch.equal(before[n], getattr(p.sw, n)), f"trial changed {n}"
+        hm.hs_commit(p.sw.ctx, trial, g, torch.zeros((R,), dtype=torch.int32, device="cuda"), cstat)
+        for n in names:
+            assert torch.equal(before[n], getattr(p.sw, n)), f"rejected commit changed {n}"
+        # the real selection, accepted for a random subset of the requests
+        hm.hs_trial(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(ids)).cuda(), None, out, miss, status, g, trial)
+        oc = _oracle_copy(p.o)
+        o_out, o_miss, o_st, o_g = oc.step(ids, gather=True)
+        assert (out.cpu().numpy() == o_out).all() and (g.cpu().numpy() == o_g).all()
+        accept = rng.integers(0, 2, size=R).astype(np.int32)
+        accept[t % R] = 1
+        hm.hs_commit(p.sw.ctx, trial, g, torch.from_numpy(accept).cuda(), cstat)
+        assert (cstat.cpu().numpy() == 0).all()
+        for r in np.nonzero(accept)[0]:
+            for n in ("slot_tok", "stamp", "page", "t", "hot"):
+                getattr(p.o, n)[r] = getattr(oc, n)[r]
+        p.t += 1
+        p.check_state()
+        # committing the same records again: every accepted request is now stale
+        hm.hs_commit(p.sw.ctx, trial, g, torch.from_numpy(accept).cuda(), cstat)
+        assert (cstat.cpu().numpy() == accept * hm.HS_STATUS_STALE).all()
+        p.check_state()
+    p.close()
+
+
+def test_trial_commit_hybrid_tail():
+    """Trial and commit with a device tail: resident ids resolve in place and take no slot."""
+    import hierarchical_memory_amd as hm
+    w = workload.HYBRID_64.with_(num_requests=4, steps=10)
+    p = Pair(w, gather=True)
+    trial = p.sw.trial_buffer()
+    out, miss, status, g = p.outs
+    for t in range(w.steps):
+        ids = p.ids[:, t]
+        hm.hs_trial(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(ids)).cuda(), p.tail0_dev, out, miss, status,
+                    g, trial)
+        o_out, o_miss, o_st, o_g = p.o.step(ids, p.tail0, gather=True)
+        assert (out.cpu().numpy() == o_out).all() and (g.cpu().numpy() == o_g).all()
+        hm.hs_commit(p.sw.ctx, trial, g)
+        p.t += 1
+        p.check_state()
+    p.close()
