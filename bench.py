@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="buffer-size sweep instead: B in {2048,4096,6144} x keep in {0.6,0.8,0.95}, 64 requests, "
                          "512 steps each; reports the 100-step rolling mean of misses per step and the resolve rate")
+    ap.add_argument("--policy", choices=["lru", "fifo", "both"], default="lru",
+                    help="eviction policy (--sweep: 'both' runs every (B, keep) under LRU and FIFO)")
     ap.add_argument("--trial-steps", type=int, default=256,
                     help="steps of the hs_trial + hs_commit leg after a reset (0: skip)")
     ap.add_argument("--split-steps", type=int, default=-1,
@@ -98,7 +100,7 @@ def link_and_hbm_probes(torch):
     return n / link_ms / 1e6, 2 * n / hbm_ms / 1e6
 
 
-def cpu_baseline(w, ids, seconds: float):
+def cpu_baseline(w, ids, seconds: float, policy: int = 0):
     """The oracle, as it is, on the first requests of the same streams (its own rows from the generator)."""
     import numpy as np
     import oracle
@@ -121,7 +123,8 @@ def cpu_baseline(w, ids, seconds: float):
     if w.tail_tokens:
         tail = np.ascontiguousarray(host[:, w.tail0:w.tail0 + w.tail_tokens])
         tail0 = np.full(n_req, w.tail0, np.int32)
-    o = oracle.Oracle(n_req, w.buffer_slots, w.top_k, w.host_rows, w.row_bytes, T=w.tail_tokens, host=host, tail=tail)
+    o = oracle.Oracle(n_req, w.buffer_slots, w.top_k, w.host_rows, w.row_bytes, T=w.tail_tokens, host=host, tail=tail,
+                      policy=policy)
     sub = np.ascontiguousarray(ids[:n_req])
     misses = 0
     t0 = time.perf_counter()
@@ -190,9 +193,11 @@ def sweep(args) -> int:
     import workload
     torch.cuda.set_device(0)
     runs = []
-    for w in workload.sweep_workloads():
+    policies = {"lru": [hm.HS_EVICT_LRU], "fifo": [hm.HS_EVICT_FIFO], "both": [hm.HS_EVICT_LRU, hm.HS_EVICT_FIFO]}
+    cases = [(w, pol) for w in workload.sweep_workloads() for pol in policies[args.policy]]
+    for w, pol in cases:
         R, k, B, H, rb = w.num_requests, w.top_k, w.buffer_slots, w.host_rows, w.row_bytes
-        sw = hm.SwapIn(hm.config(R, k, B, 0.0, rb, H, 0))
+        sw = hm.SwapIn(hm.config(R, k, B, 0.0, rb, H, 0, pol))
         workload.fill_rows_ptr(sw.host_pool_address(), 0, R * H, w.row_elems, w.row_seed)
         ids = workload.streams(w)
         topk = torch.from_numpy(np.ascontiguousarray(ids.transpose(1, 0, 2))).cuda()
@@ -217,13 +222,14 @@ def sweep(args) -> int:
         roll = np.convolve(m, np.ones(100) / 100, mode="valid")          # step 99 onwards
         n = w.steps - W
         timed_miss = miss[W:].cpu().numpy().astype(np.int64).sum()
-        run = {"buffer_slots": B, "keep": w.keep_permille / 1000, "steps": w.steps,
+        run = {"policy": "fifo" if pol == hm.HS_EVICT_FIFO else "lru", "buffer_slots": B,
+               "keep": w.keep_permille / 1000, "steps": w.steps,
                "miss_per_request_step_rolling100_at": {str(t): round(float(roll[t - 99]), 2)
                                                       for t in (99, 199, 299, 399, w.steps - 1)},
                "miss_per_request_step_mean_after_step_99": round(float(m[99:].mean()), 2),
                "entries_per_s": n * R * k / (ms / 1e3), "ms_per_step": ms / n,
                "miss_copy_GBps": timed_miss * rb / (ms / 1e3) / 1e9}
-        log(f"[sweep] B={B} keep={w.keep_permille / 1000}: misses/request-step {run['miss_per_request_step_mean_after_step_99']}"
+        log(f"[sweep] {run['policy']} B={B} keep={w.keep_permille / 1000}: misses/request-step {run['miss_per_request_step_mean_after_step_99']}"
             f", {run['ms_per_step']:.3f} ms/step, {run['entries_per_s'] / 1e6:.0f} M entries/s")
         runs.append(run)
         sw.close()
@@ -304,7 +310,8 @@ def main() -> int:
 
     log(f"[bench] {w.name}: R={R} k={k} B={B} host_rows={H} T={T}, warmup {W} + timed {K} steps")
     t0 = time.perf_counter()
-    sw = hm.SwapIn(hm.config(R, k, B, 0.0, rb, H, T))
+    policy = hm.HS_EVICT_FIFO if args.policy == "fifo" else hm.HS_EVICT_LRU
+    sw = hm.SwapIn(hm.config(R, k, B, 0.0, rb, H, T, policy))
     workload.fill_rows_ptr(sw.host_pool_address(), 0, R * H, w.row_elems, w.row_seed)
     tail0 = None
     if T:
@@ -372,6 +379,7 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "requests": R, "top_k": k, "buffer_slots": B, "host_rows": H,
                    "tail_tokens": T, "row_bytes": rb, "fused_gather": w.fused_gather,
+                   "eviction_policy": "fifo" if policy == hm.HS_EVICT_FIFO else "lru",
                    "timed_steps": [W, W + K]},
         "miss_copy_GBps": miss_gbps,
         "miss_rows_per_request_step": total_miss / (K * R),
@@ -396,7 +404,7 @@ def main() -> int:
     del topk
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline ...")
-        rep["cpu_baseline"] = cpu_baseline(w, ids, args.cpu_seconds)
+        rep["cpu_baseline"] = cpu_baseline(w, ids, args.cpu_seconds, policy)
         log(f"[bench] CPU oracle: {rep['cpu_baseline']['value'] / 1e6:.2f} M entries/s ({rep['cpu_baseline']['sample']})")
     print(json.dumps(rep), flush=True)
     return 0

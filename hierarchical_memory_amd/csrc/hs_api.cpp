@@ -55,6 +55,9 @@ int check_config(const hs_config* cfg, int32_t* H_out, hs::Layout* L_out) {
     return fail(HS_E_INVALID, "row_bytes must be a multiple of 16 in [16, 1 MiB] (got %d)", cfg->row_bytes);
   if (cfg->tail_tokens < 0) return fail(HS_E_INVALID, "tail_tokens must be >= 0 (got %d)", cfg->tail_tokens);
   if (cfg->max_context < 0) return fail(HS_E_INVALID, "max_context must be >= 0 (got %d)", cfg->max_context);
+  if (cfg->eviction_policy != HS_EVICT_LRU && cfg->eviction_policy != HS_EVICT_FIFO)
+    return fail(HS_E_INVALID, "eviction_policy must be HS_EVICT_LRU (0) or HS_EVICT_FIFO (1) (got %d)",
+                cfg->eviction_policy);
   int64_t H = cfg->max_context;
   if (H == 0) {
     const double want = std::ceil((double)cfg->host_to_device_ratio * (double)cfg->device_buffer_size);
@@ -253,6 +256,7 @@ int resolve_common(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, i
   a.H = ctx->H;
   a.T = ctx->cfg.tail_tokens;
   a.row16 = ctx->cfg.row_bytes / 16;
+  a.policy = ctx->cfg.eviction_policy;
   a.L = ctx->layout;
   a.host = (const hs::v4u*)ctx->pool_dev;
   a.hot = (hs::v4u*)ctx->views.hot;

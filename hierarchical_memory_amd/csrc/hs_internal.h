@@ -54,6 +54,7 @@ inline Layout make_layout(int k, int B, int H) {
 
 struct ResolveArgs {
   int32_t R, k, B, H, T, row16;
+  int32_t policy;   // 0 LRU, 1 FIFO
   Layout L;
   const v4u* host;  // device address of the pinned pool [R][H][row16]
   v4u* hot;         // [R][B][row16]

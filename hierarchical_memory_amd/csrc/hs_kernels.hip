@@ -37,6 +37,10 @@
 // every hit or victim slot now carries stamp t, larger than any older stamp, so
 // appending them in slot order keeps the list sorted. Empty slots (stamp -1)
 // start at the front in slot order after a reset.
+//
+// FIFO replacement (the alternative to LRU a request can be configured with)
+// takes victims the same way, but a hit does not refresh its stamp: hits keep
+// their place in the list and only the victims, stamped t, move to its end.
 #include "hs_internal.h"
 
 #include <climits>
@@ -141,6 +145,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   const int k = a.k, B = a.B, H = a.H, T = a.T;
   const int W = (int)L.words;
   const bool has_tail = a.tail0 != nullptr;
+  const bool fifo = a.policy == 1;  // else LRU
   const int32_t t0 = has_tail ? a.tail0[r] : 0;
   const int32_t t = a.step[r];
   const size_t rk = (size_t)r * k, rB = (size_t)r * B, rH = (size_t)r * H;
@@ -317,15 +322,20 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       mpre[w] = (uint16_t)run;
       run += __popc(cbits[w] & ~hbits[w]);
     }
+    // LRU: the new order opens with the candidates that stay; FIFO: with every slot that stays (hits keep
+    // their place), position p moving up by the number of victims before it
     int runC = (int)((uint32_t)pre >> 16);
     for (int p = s0; p < s1; ++p) {
       const int slot = ord[p];
-      if (sflag[slot] & 1) continue;
+      if (sflag[slot] & 1) {
+        if (fifo) new_order[p - min(m, runC)] = (uint16_t)slot;
+        continue;
+      }
       if (runC < m) {
         vict[runC] = slot;
         sflag[slot] = 2;
       } else {
-        new_order[runC - m] = (uint16_t)slot;
+        new_order[fifo ? p - m : runC - m] = (uint16_t)slot;
       }
       ++runC;
     }
@@ -368,15 +378,16 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     a.out[rk + i] = o;
     gsrc[i] = g;
   }
-  // hit and victim slots close the new LRU order, in slot order (the scan's barrier also publishes the
-  // LDS writes above)
+  // the slots used this step close the new order in slot order: hits and victims (LRU) or victims only
+  // (FIFO); the scan's barrier also publishes the LDS writes above
+  const int tail_start = fifo ? B - m : ncand - m;
   {
     int ch = 0;
-    for (int s = s0; s < s1; ++s) ch += sflag[s] != 0;
+    for (int s = s0; s < s1; ++s) ch += fifo ? sflag[s] == 2 : sflag[s] != 0;
     int tot;
-    int pos = (ncand - m) + block_excl_scan(ch, misc + kMiscScanTail, lane, wave, &tot);
+    int pos = tail_start + block_excl_scan(ch, misc + kMiscScanTail, lane, wave, &tot);
     for (int s = s0; s < s1; ++s) {
-      if (sflag[s] == 0) continue;
+      if (fifo ? sflag[s] != 2 : sflag[s] == 0) continue;
       if (pos < B) new_order[pos] = (uint16_t)s;  // pos < B always holds for a permutation
       ++pos;
     }
@@ -386,7 +397,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   if (kMode != kTrial) {
     for (int s = tid; s < B; s += kThreads) {
       const uint8_t f = sflag[s];
-      if (f) a.stamp[rB + s] = t;
+      if (fifo ? f == 2 : f != 0) a.stamp[rB + s] = t;
       if (f == 2) a.slot_tok[rB + s] = stok[s];
     }
   }
@@ -404,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     return;
   }
 
-  if (kMode == kTrial && tid == 0) trial_header(a, r, m, ncand - m, t);
+  if (kMode == kTrial && tid == 0) trial_header(a, r, m, tail_start, t);
 
   // ---- phase 6: rows (the block scan above ended with a barrier, so mtok and gsrc are visible)
   const int row16 = a.row16;

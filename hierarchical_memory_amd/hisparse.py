@@ -18,6 +18,7 @@ _lib = None
 
 HS_OK, HS_E_INVALID, HS_E_NOMEM, HS_E_HIP, HS_E_STATE = 0, -1, -2, -3, -4
 HS_STATUS_BAD_ID, HS_STATUS_DUP_ID, HS_STATUS_BAD_STATE, HS_STATUS_STALE = 1, 2, 4, 8
+HS_EVICT_LRU, HS_EVICT_FIFO = 0, 1
 
 EXPORTED = ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
             "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_gather", "hs_rebuild_order", "hs_destroy",
@@ -33,7 +34,7 @@ class HiSparseError(RuntimeError):
 class HsConfig(ctypes.Structure):
     _fields_ = [("num_requests", ctypes.c_int32), ("top_k", ctypes.c_int32), ("device_buffer_size", ctypes.c_int32),
                 ("host_to_device_ratio", ctypes.c_float), ("row_bytes", ctypes.c_int32),
-                ("max_context", ctypes.c_int32), ("tail_tokens", ctypes.c_int32)]
+                ("max_context", ctypes.c_int32), ("tail_tokens", ctypes.c_int32), ("eviction_policy", ctypes.c_int32)]
 
 
 class HsDeviceViews(ctypes.Structure):
@@ -98,8 +99,10 @@ def _check(rc: int) -> None:
 
 
 def config(num_requests: int, top_k: int, device_buffer_size: int, host_to_device_ratio: float = 0.0,
-           row_bytes: int = 1152, max_context: int = 0, tail_tokens: int = 0) -> HsConfig:
-    return HsConfig(num_requests, top_k, device_buffer_size, host_to_device_ratio, row_bytes, max_context, tail_tokens)
+           row_bytes: int = 1152, max_context: int = 0, tail_tokens: int = 0,
+           eviction_policy: int = HS_EVICT_LRU) -> HsConfig:
+    return HsConfig(num_requests, top_k, device_buffer_size, host_to_device_ratio, row_bytes, max_context, tail_tokens,
+                    eviction_policy)
 
 
 def config_from_hisparse_json(spec: Union[str, Dict[str, Any]], num_requests: int, row_bytes: int = 1152,

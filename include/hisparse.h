@@ -77,7 +77,17 @@ typedef struct hs_config {
   int32_t row_bytes;          /* bytes per KV row, a positive multiple of 16 (576 bf16 = 1152) */
   int32_t max_context;        /* > 0: host rows per request (overrides the ratio) */
   int32_t tail_tokens;        /* T >= 0: device-resident tail rows per request (Mixed residency) */
+  int32_t eviction_policy;    /* HS_EVICT_LRU (default) or HS_EVICT_FIFO */
 } hs_config;
+
+/*
+ * Eviction policies. LRU is the method's ("HiSparse: Turbocharging Sparse Attention with Hierarchical
+ * Memory", section 2). The pages compare it with another strategy they do not name; FIFO is offered as
+ * that alternative: victims are taken the same way, but a hit does not refresh its slot's stamp, so a
+ * slot's stamp is the step it was filled.
+ */
+#define HS_EVICT_LRU 0
+#define HS_EVICT_FIFO 1
 
 /*
  * Device buffers (caller-owned). Sizes are in bytes and must be at least what

@@ -22,6 +22,8 @@ _lib = None
 
 BAD_ID = 1
 DUP_ID = 2
+LRU = 0
+FIFO = 1
 
 
 def build(force: bool = True, src: str = _SRC, dst: str = _LIB_PATH) -> str:
@@ -35,7 +37,7 @@ def build(force: bool = True, src: str = _SRC, dst: str = _LIB_PATH) -> str:
 
 class Dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("k", ctypes.c_int32), ("H", ctypes.c_int32), ("T", ctypes.c_int32),
-                ("row_bytes", ctypes.c_int64)]
+                ("row_bytes", ctypes.c_int64), ("policy", ctypes.c_int32)]
 
 
 def load(path: Optional[str] = None):
@@ -69,9 +71,11 @@ class Oracle:
     """
 
     def __init__(self, n: int, B: int, k: int, H: int, row_bytes: int, T: int = 0,
-                 host: Optional[np.ndarray] = None, tail: Optional[np.ndarray] = None, lib_path: Optional[str] = None):
+                 host: Optional[np.ndarray] = None, tail: Optional[np.ndarray] = None, lib_path: Optional[str] = None,
+                 policy: int = LRU):
         self.n, self.B, self.k, self.H, self.T, self.rb = n, B, k, H, T, row_bytes
-        self.dims = Dims(B, k, H, T, row_bytes)
+        self.policy = policy
+        self.dims = Dims(B, k, H, T, row_bytes, policy)
         self.lib = load(lib_path)
         self.slot_tok = np.full((n, B), -1, np.int32)
         self.stamp = np.full((n, B), -1, np.int32)

@@ -24,6 +24,12 @@
  *   - the stamp of a hit slot and of a newly filled slot becomes the step t.
  * With these rules the outcome is unique.
  *
+ * The pages compare LRU with another eviction strategy they do not name
+ * ("HiSparse: Turbocharging Sparse Attention with Hierarchical Memory",
+ * section 2, and the Japanese review, section 「効率的なSwap-inカーネル」). The
+ * model also runs FIFO as that alternative: the same steps, except that a hit
+ * leaves its slot's stamp alone, so a slot's stamp is the step it was filled.
+ *
  * Invalid ids never trap: -1 is padding (output -1, no effect), an id outside
  * [0, host_rows) or at/after tail0 but outside the tail window sets
  * ORACLE_BAD_ID, a repeat of an earlier valid id in the same step sets
@@ -36,12 +42,16 @@
 #define ORACLE_BAD_ID 1
 #define ORACLE_DUP_ID 2
 
+#define ORACLE_LRU 0
+#define ORACLE_FIFO 1
+
 typedef struct {
   int32_t B;          /* hot slots per request */
   int32_t k;          /* selected ids per step */
   int32_t H;          /* host rows per request */
   int32_t T;          /* device-resident tail rows per request (0: none) */
   int64_t row_bytes;  /* bytes per KV row */
+  int32_t policy;     /* ORACLE_LRU or ORACLE_FIFO */
 } oracle_dims;
 
 typedef struct { int32_t key; int32_t val; } pair_t;
@@ -134,9 +144,10 @@ int oracle_resolve(const oracle_dims* d, int32_t* slot_tok, int32_t* stamp, int3
     memcpy(hot + (int64_t)v * rb, host + (int64_t)x * rb, (size_t)rb);
     out[misses[j].val] = v;
   }
-  /* hit slots were used at step t too */
-  for (int32_t s = 0; s < B; ++s)
-    if (hit[s]) stamp[s] = t;
+  /* LRU: hit slots were used at step t too; FIFO: a slot keeps the step it was filled */
+  if (d->policy == ORACLE_LRU)
+    for (int32_t s = 0; s < B; ++s)
+      if (hit[s]) stamp[s] = t;
 
   *miss_out = m;
   *status_out = status;

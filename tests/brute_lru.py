@@ -19,8 +19,11 @@ BAD_ID, DUP_ID = 1, 2
 
 
 class ListLRU:
-    def __init__(self, B: int, H: int, T: int = 0):
-        self.B, self.H, self.T = B, H, T
+    """fifo=True: the same list, but a hit does not move its slot (FIFO replacement): only newly filled slots
+    go to the back, and a slot's last-use step is the step it was filled."""
+
+    def __init__(self, B: int, H: int, T: int = 0, fifo: bool = False):
+        self.B, self.H, self.T, self.fifo = B, H, T, fifo
         self.reset()
 
     def reset(self) -> None:
@@ -70,9 +73,13 @@ class ListLRU:
             self.holder[v] = x
             self.where[x] = v
             out[i] = v
-            used_slots.add(v)
-        self.order = free_order[len(missed):] + sorted(used_slots)
-        for s in used_slots:
+        if self.fifo:
+            moved = set(victims)
+            self.order = [s for s in self.order if s not in moved] + sorted(moved)
+        else:
+            moved = used_slots | set(victims)
+            self.order = free_order[len(missed):] + sorted(moved)
+        for s in moved:
             self.last_used[s] = self.t
         self.t += 1
         return out, len(missed), status

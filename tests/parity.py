@@ -32,7 +32,8 @@ def order_sorted_by_stamp(order: np.ndarray, stamp: np.ndarray) -> bool:
 
 class Pair:
     def __init__(self, w: workload.Workload, sample: Optional[Sequence[int]] = None, gather: Optional[bool] = None,
-                 n_steps: Optional[int] = None, ids: Optional[np.ndarray] = None, tail0: Optional[np.ndarray] = None):
+                 n_steps: Optional[int] = None, ids: Optional[np.ndarray] = None, tail0: Optional[np.ndarray] = None,
+                 policy: int = 0):
         self.w = w
         self.R, self.k, self.B, self.H = w.num_requests, w.top_k, w.buffer_slots, w.host_rows
         self.T, self.rb = w.tail_tokens, w.row_bytes
@@ -41,7 +42,7 @@ class Pair:
         self.n_steps = (w.steps if ids is None else ids.shape[1]) if n_steps is None else n_steps
         log(f"[pair] {w.name}: R={self.R} k={self.k} B={self.B} H={self.H} T={self.T} steps={self.n_steps} "
             f"sample={self.sample[:8]}{'...' if len(self.sample) > 8 else ''}")
-        cfg = hm.config(self.R, self.k, self.B, 0.0, self.rb, self.H, self.T)
+        cfg = hm.config(self.R, self.k, self.B, 0.0, self.rb, self.H, self.T, policy)
         self.sw = hm.SwapIn(cfg)
         workload.fill_rows_ptr(self.sw.host_pool_address(), 0, self.R * self.H, w.row_elems, w.row_seed)
         self.tail0_dev = None
@@ -70,7 +71,7 @@ class Pair:
                 a = int(self.tail0[r])
                 m = max(0, min(self.T, self.H - a))
                 tail_o[j, :m] = host_o[j, a:a + m]
-        self.o = oracle.Oracle(n, self.B, self.k, self.H, self.rb, T=self.T, host=host_o, tail=tail_o)
+        self.o = oracle.Oracle(n, self.B, self.k, self.H, self.rb, T=self.T, host=host_o, tail=tail_o, policy=policy)
         self.ids = workload.streams(w, n_steps=self.n_steps) if ids is None else np.ascontiguousarray(ids, np.int32)
         self.sample_t = torch.tensor(self.sample, dtype=torch.long, device="cuda")
         self.outs = self.sw.outputs(self.gather)

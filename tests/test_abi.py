@@ -41,10 +41,11 @@ def test_every_declared_symbol_is_exported():
     (dict(tail_tokens=-1), "tail_tokens"),
     (dict(max_context=-5), "max_context"),
     (dict(device_buffer_size=40000, max_context=1 << 20), "LDS"),
+    (dict(eviction_policy=2), "eviction_policy"),
 ])
 def test_bad_config_rejected(kw, msg):
     base = dict(num_requests=4, top_k=256, device_buffer_size=512, host_to_device_ratio=8.0, row_bytes=1152,
-                max_context=0, tail_tokens=0)
+                max_context=0, tail_tokens=0, eviction_policy=0)
     base.update(kw)
     cfg = hm.HsConfig(**base)
     with pytest.raises(hm.HiSparseError) as e:

@@ -403,3 +403,39 @@ def test_trial_commit_hybrid_tail():
         p.t += 1
         p.check_state()
     p.close()
+
+
+FIFO_CASES = [workload.SINGLE_4K, workload.GROW_32.with_(num_requests=8, steps=64),
+              workload.HYBRID_64.with_(num_requests=4, steps=24),
+              workload.SWEEP_BASE.with_(num_requests=4, steps=48, buffer_slots=2048)]
+
+
+@pytest.mark.parametrize("w", FIFO_CASES, ids=lambda w: w.name)
+def test_fifo_policy(w):
+    """FIFO replacement (hits do not refresh stamps) against the oracle run with the same policy."""
+    import hierarchical_memory_amd as hm
+    p = Pair(w, policy=hm.HS_EVICT_FIFO)
+    p.run(check_every=4)
+    p.close()
+
+
+def test_fifo_plan_trial_commit():
+    import hierarchical_memory_amd as hm
+    w = workload.GROW_32.with_(num_requests=4, steps=16)
+    p = Pair(w, policy=hm.HS_EVICT_FIFO, gather=True)
+    plan, trial = p.sw.plan_buffer(), p.sw.trial_buffer()
+    out, miss, status, g = p.outs
+    for t in range(w.steps):
+        ids = np.ascontiguousarray(p.ids[:, t])
+        topk = torch.from_numpy(ids).cuda()
+        if t % 2:
+            hm.hs_plan(p.sw.ctx, topk, None, out, miss, status, plan)
+            hm.hs_copy(p.sw.ctx, plan, miss)
+        else:
+            hm.hs_trial(p.sw.ctx, topk, None, out, miss, status, g, trial)
+            hm.hs_commit(p.sw.ctx, trial, g)
+        o_out, o_miss, _, _ = p.o.step(ids)
+        assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+        p.t += 1
+        p.check_state()
+    p.close()

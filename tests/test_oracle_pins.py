@@ -58,7 +58,11 @@ def check_invariants(o: oracle.Oracle, r: int, ids, out, miss, status, tail0=Non
     for i, x in enumerate(ids):
         v = out[i]
         if 0 <= v < B:
-            assert st_[v] == x and page[x] == v and stamp[v] == o.t[r] - 1
+            assert st_[v] == x and page[x] == v
+            if o.policy == oracle.LRU:
+                assert stamp[v] == o.t[r] - 1
+            else:
+                assert stamp[v] <= o.t[r] - 1
         elif v >= B:
             assert tail0 is not None and v == B + x - tail0
         if gathered is not None:
@@ -110,9 +114,10 @@ def _compare_with_list(o, lru, r, ids, tail0=None):
     check_invariants(o, r, ids, out[0].tolist(), miss[0], status[0], tail0)
 
 
-def test_list_lru_exhaustive_tiny():
+@pytest.mark.parametrize("policy", [oracle.LRU, oracle.FIFO], ids=["lru", "fifo"])
+def test_list_lru_exhaustive_tiny(policy):
     """Every sequence of 3 steps of k-subsets of 6 tokens (k <= 3), every B in [k, 4], with the ids of each
-    step in two orders: the oracle and the list LRU agree on every output and every table."""
+    step in two orders: the oracle and the list model agree on every output and every table."""
     H = 6
     rb = 16
     host = make_host(1, H, rb)
@@ -122,8 +127,8 @@ def test_list_lru_exhaustive_tiny():
         for B in range(k, 5):
             for seq in itertools.product(subsets, repeat=3):
                 for flip in (False, True):
-                    o = oracle.Oracle(1, B, k, H, rb, host=host)
-                    lru = ListLRU(B, H)
+                    o = oracle.Oracle(1, B, k, H, rb, host=host, policy=policy)
+                    lru = ListLRU(B, H, fifo=policy == oracle.FIFO)
                     for ids in seq:
                         ids = ids[::-1] if flip else ids
                         _compare_with_list(o, lru, 0, ids)
@@ -142,8 +147,9 @@ def test_list_lru_random(data):
     use_tail = data.draw(st.booleans()) and T > 0
     tail0 = data.draw(st.integers(0, H)) if use_tail else None
     steps = data.draw(st.integers(1, 8))
-    o = oracle.Oracle(1, B, k, H, 16, T=T, host=make_host(1, H, 16))
-    lru = ListLRU(B, H, T)
+    policy = data.draw(st.sampled_from([oracle.LRU, oracle.FIFO]))
+    o = oracle.Oracle(1, B, k, H, 16, T=T, host=make_host(1, H, 16), policy=policy)
+    lru = ListLRU(B, H, T, fifo=policy == oracle.FIFO)
     for _ in range(steps):
         ids = data.draw(st.lists(st.integers(-3, H + 2), min_size=k, max_size=k))
         _compare_with_list(o, lru, 0, ids, tail0)
@@ -210,6 +216,34 @@ def test_buffer_equals_topk():
             for j, x in enumerate(new):
                 assert out[0][cur.index(x)] == free[j]
         prev_slots = {x: int(out[0][i]) for i, x in enumerate(cur)}
+
+
+def test_fifo_closed_forms():
+    """FIFO: a hit never refreshes a stamp. Keeping the whole set, stamps stay at the step the slots were
+    filled (0); with a buffer holding the whole context, a token's slot is the same as under LRU (only
+    compulsory misses) but its stamp is the first step that selected it."""
+    w = workload.SINGLE_4K.with_(keep_permille=1000)
+    ids = workload.streams(w)[0]
+    o = oracle.Oracle(1, w.buffer_slots, w.top_k, w.host_rows, 16, host=make_host(1, w.host_rows, 16),
+                      policy=oracle.FIFO)
+    for t in range(w.steps):
+        out, miss, status, _ = o.step(ids[t][None])
+        assert miss[0] == (w.top_k if t == 0 else 0)
+        occ = o.slot_tok[0] >= 0
+        assert (o.stamp[0][occ] == 0).all() and (o.stamp[0][~occ] == -1).all()
+    w = workload.SINGLE_4K.with_(buffer_slots=4096)
+    ids = workload.streams(w)[0]
+    lru = oracle.Oracle(1, 4096, w.top_k, w.host_rows, 16, host=make_host(1, w.host_rows, 16))
+    fifo = oracle.Oracle(1, 4096, w.top_k, w.host_rows, 16, host=make_host(1, w.host_rows, 16), policy=oracle.FIFO)
+    first = {}
+    for t in range(w.steps):
+        a = lru.step(ids[t][None])[0]
+        b = fifo.step(ids[t][None])[0]
+        assert (a == b).all()
+        for x in ids[t].tolist():
+            first.setdefault(x, t)
+    for s in np.nonzero(fifo.slot_tok[0] >= 0)[0]:
+        assert fifo.stamp[0][s] == first[int(fifo.slot_tok[0][s])]
 
 
 def test_same_set_every_step():
@@ -294,6 +328,8 @@ MUTANTS = {
     "tail window not checked": ("if (resident && (int64_t)x - (int64_t)tail0 >= (int64_t)T)", "if (0)"),
     "tail index off by one": ("out[i] = B + (x - tail0);", "out[i] = B + (x - tail0) + 1;"),
     "step counter not advanced": ("*t_io = t + 1;", "*t_io = t;"),
+    "FIFO refreshes hit stamps": ("if (d->policy == ORACLE_LRU)\n    for", "if (1)\n    for"),
+    "LRU leaves hit stamps alone": ("if (d->policy == ORACLE_LRU)\n    for", "if (d->policy == ORACLE_FIFO)\n    for"),
 }
 
 
@@ -316,9 +352,17 @@ def _run_pins_against(lib_path: str) -> bool:
                     lru = ListLRU(B, 6)
                     for ids in seq:
                         _compare_with_list(o, lru, 0, list(ids)[::-1])
+        for k in (1, 2, 3):
+            for B in range(k, 5):
+                for seq in itertools.product(list(itertools.combinations(range(6), k)), repeat=2):
+                    o = oracle.Oracle(1, B, k, 6, 16, host=host, policy=oracle.FIFO)
+                    lst = ListLRU(B, 6, fifo=True)
+                    for ids in seq:
+                        _compare_with_list(o, lst, 0, list(ids)[::-1])
         me.test_cold_start()
         me.test_buffer_equals_topk()
         me.test_error_paths()
+        me.test_fifo_closed_forms()
         rng = random.Random(5)
         for _ in range(200):
             k = rng.randint(1, 8); B = rng.randint(k, 12); H = rng.randint(2, 24); T = rng.randint(0, 4)
