@@ -2,6 +2,7 @@
 #include "hisparse.h"
 #include "hs_internal.h"
 
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -257,6 +258,14 @@ int resolve_common(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, i
   a.T = ctx->cfg.tail_tokens;
   a.row16 = ctx->cfg.row_bytes / 16;
   a.policy = ctx->cfg.eviction_policy;
+  // fused row copy: about 128K 16-byte host loads in flight over the whole chip saturate the host link
+  // (measured: more in flight only queues); at most 1024 threads per request, then up to 4 loads each
+  {
+    const int per_request = (131072 + a.R - 1) / a.R;
+    a.copy_threads = per_request < 256 ? 256 : per_request > hs::kThreads ? hs::kThreads : per_request;
+    const int u = (per_request + hs::kThreads - 1) / hs::kThreads;
+    a.copy_unroll = u <= 1 ? 1 : u == 2 ? 2 : 4;
+  }
   a.L = ctx->layout;
   a.host = (const hs::v4u*)ctx->pool_dev;
   a.hot = (hs::v4u*)ctx->views.hot;
@@ -367,6 +376,30 @@ int hs_gather(hs_ctx* ctx, const int32_t* d_out, void* d_gather, void* stream) {
   a.gather = (hs::v4u*)d_gather;
   hipError_t e = hs::launch_gather(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "gather launch");
+  return ok();
+}
+
+int hs_offload(hs_ctx* ctx, const void* d_rows, const int32_t* d_pos, int32_t n, int32_t* d_status, void* stream) {
+  int rc = check_ready(ctx);
+  if (rc) return rc;
+  if (n < 0) return fail(HS_E_INVALID, "n must be >= 0 (got %d)", n);
+  if (n > 0 && (!d_rows || !d_pos)) return fail(HS_E_INVALID, "rows and pos must not be NULL");
+  if (d_rows && !aligned(d_rows, 16)) return fail(HS_E_INVALID, "rows are not 16-byte aligned");
+  if ((int64_t)n * (ctx->cfg.row_bytes / 16) > INT32_MAX) return fail(HS_E_INVALID, "n is too large");
+  hs::OffloadArgs a{};
+  a.R = ctx->cfg.num_requests;
+  a.B = ctx->cfg.device_buffer_size;
+  a.H = ctx->H;
+  a.row16 = ctx->cfg.row_bytes / 16;
+  a.n = n;
+  a.rows = (const hs::v4u*)d_rows;
+  a.pos = d_pos;
+  a.status = d_status;
+  a.host = (hs::v4u*)ctx->pool_dev;
+  a.hot = (hs::v4u*)ctx->views.hot;
+  a.page = ctx->views.page;
+  hipError_t e = hs::launch_offload(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "offload launch");
   return ok();
 }
 

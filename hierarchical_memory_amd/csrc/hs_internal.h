@@ -13,10 +13,11 @@ constexpr int kMaxSlots = 65535;          // slot ids fit the uint16 LRU order l
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte chunk of a row
 
-// LDS carve-up of one resolve workgroup (byte offsets; every section 16-byte aligned).
-// Sections reused once dead: the rank -> first position table holds the victim list from phase 4 on,
-// the per-position ranks hold the missed ids from phase 5 on, and the prefix counts of the selected set
-// become the prefix counts of the misses.
+// LDS carve-up of one resolve workgroup (byte offsets; every section 16-byte aligned). The token sets are
+// kept as separate arrays of 32-bit words (consecutive words in consecutive LDS banks, which spreads the
+// random lookups). Sections reused once dead: the rank -> first position table holds the victim list from
+// phase 4 on, the per-position ranks hold the missed ids from phase 5 on, and the prefix counts of the
+// selected set become the prefix counts of the misses.
 struct Layout {
   uint32_t ids, cls, pos_slot, rank, stok, ord, sflag, sel, cbits, hbits, selpre, first, mpre, vict, mtok, gsrc,
       misc;
@@ -38,10 +39,10 @@ inline Layout make_layout(int k, int B, int H) {
   L.stok = take(4ull * B);
   L.ord = take(2ull * B);
   L.sflag = take(1ull * B);
-  L.sel = take(4ull * L.words);    // selected ids (candidates and resident)
-  L.cbits = take(4ull * L.words);  // candidate ids (not resident)
-  L.hbits = take(4ull * L.words);  // candidate ids found in a slot
-  L.selpre = take(2ull * L.words); // uint16 prefix counts (k <= 8192)
+  L.sel = take(4ull * L.words);     // selected ids (candidates and resident)
+  L.cbits = take(4ull * L.words);   // candidate ids (not resident)
+  L.hbits = take(4ull * L.words);   // candidate ids found in a slot
+  L.selpre = take(2ull * L.words);  // uint16 prefix counts (k <= 8192)
   L.first = take(4ull * k);
   L.mpre = L.selpre;
   L.vict = L.first;
@@ -55,6 +56,7 @@ inline Layout make_layout(int k, int B, int H) {
 struct ResolveArgs {
   int32_t R, k, B, H, T, row16;
   int32_t policy;   // 0 LRU, 1 FIFO
+  int32_t copy_threads, copy_unroll;  // fused row copy: threads per workgroup and loads in flight each
   Layout L;
   const v4u* host;  // device address of the pinned pool [R][H][row16]
   v4u* hot;         // [R][B][row16]
@@ -102,6 +104,16 @@ struct CopyArgs {
   v4u* hot;
 };
 
+struct OffloadArgs {
+  int32_t R, B, H, row16, n;
+  const v4u* rows;     // [R][n][row16] device rows
+  const int32_t* pos;  // [R] first token of each request's rows
+  int32_t* status;     // [R] or nullptr
+  v4u* host;           // device address of the pinned pool
+  v4u* hot;
+  const int32_t* page;
+};
+
 struct RebuildArgs {
   int32_t R, B;
   const int32_t* stamp;
@@ -132,6 +144,7 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_rebuild_order(const RebuildArgs& a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
+hipError_t launch_offload(const OffloadArgs& a, hipStream_t s);
 hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes);
 
 }  // namespace hs

@@ -52,7 +52,7 @@ namespace {
 enum : int8_t { C_PAD = 0, C_BAD = 1, C_DUP = 2, C_RES = 3, C_CAND = 4 };
 
 constexpr int kStatusBadId = 1, kStatusDupId = 2, kStatusBadState = 4, kStatusStale = 8;
-constexpr int kUnroll = 4;  // 16-byte loads each thread keeps in flight in the copy loops
+constexpr int kUnroll = 4;  // 16-byte loads each thread keeps in flight in the gather loop
 
 // misc words in LDS: one slot array of wave totals per block scan, then the status word
 constexpr int kMiscScanSel = 0, kMiscScanRank = kWaves, kMiscScanTail = 2 * kWaves, kMiscStatus = 3 * kWaves;
@@ -89,6 +89,31 @@ __device__ __forceinline__ uint32_t below(int32_t x) { return (1u << (x & 31)) -
 
 __device__ __forceinline__ v4u load_host(const v4u* p) { return __builtin_nontemporal_load(p); }
 
+// Missed rows from the host pool into their slots, flattened over (miss, 16-byte chunk): thread tid of nt
+// copies chunks tid, tid + nt, ..., keeping U loads in flight.
+template <int U>
+__device__ __forceinline__ void copy_missed_rows(const v4u* hostr, v4u* hotr, const int32_t* mtok, const int32_t* vict,
+                                                 int total, int row16, int tid, int nt) {
+  for (int c0 = tid; c0 < total; c0 += nt * U) {
+    v4u v[U];
+    size_t dst[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * nt;
+      if (c < total) {
+        const int j = c / row16, q = c - j * row16;
+        v[u] = load_host(hostr + (size_t)mtok[j] * row16 + q);
+        dst[u] = (size_t)vict[j] * row16 + q;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * nt;
+      if (c < total) hotr[dst[u]] = v[u];
+    }
+  }
+}
+
 constexpr int kFused = 0, kPlan = 1, kTrial = 2;
 constexpr int kTrialHead = 4;
 
@@ -114,7 +139,8 @@ __device__ __forceinline__ void trial_header(const ResolveArgs& a, int r, int m,
 //   kTrial: commit nothing; write a trial record (the new LRU order and, per miss, token, victim slot,
 //           evicted token and position) and gather every selected row, the missed ones straight from the
 //           host pool; commit_kernel applies accepted records later (hs_trial / hs_commit).
-template <int kMode>
+// kFifo: FIFO replacement instead of LRU (hits keep their stamps and their place in the order list).
+template <int kMode, bool kFifo>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Layout& L = a.L;
@@ -129,8 +155,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   uint32_t* cbits = (uint32_t*)(smem + L.cbits);
   uint32_t* hbits = (uint32_t*)(smem + L.hbits);
   uint16_t* selpre = (uint16_t*)(smem + L.selpre);
-  int32_t* first = (int32_t*)(smem + L.first);        // rank -> lowest position holding that id
   uint16_t* mpre = (uint16_t*)(smem + L.mpre);
+  int32_t* first = (int32_t*)(smem + L.first);        // rank -> lowest position holding that id
   int32_t* vict = (int32_t*)(smem + L.vict);
   int32_t* mtok = (int32_t*)(smem + L.mtok);
   int32_t* gsrc = (int32_t*)(smem + L.gsrc);
@@ -145,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   const int k = a.k, B = a.B, H = a.H, T = a.T;
   const int W = (int)L.words;
   const bool has_tail = a.tail0 != nullptr;
-  const bool fifo = a.policy == 1;  // else LRU
+  constexpr bool fifo = kFifo;
   const int32_t t0 = has_tail ? a.tail0[r] : 0;
   const int32_t t = a.step[r];
   const size_t rk = (size_t)r * k, rB = (size_t)r * B, rH = (size_t)r * H;
@@ -422,24 +448,13 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   const v4u* hostr = a.host + rH * (size_t)row16;
   v4u* hotr = a.hot + rB * (size_t)row16;
   if (a.gather == nullptr) {
-    const int total = m * row16;
-    for (int c0 = tid; c0 < total; c0 += kThreads * kUnroll) {
-      v4u v[kUnroll];
-      size_t dst[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * kThreads;
-        if (c < total) {
-          const int j = c / row16, q = c - j * row16;
-          v[u] = load_host(hostr + (size_t)mtok[j] * row16 + q);
-          dst[u] = (size_t)vict[j] * row16 + q;
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * kThreads;
-        if (c < total) hotr[dst[u]] = v[u];
-      }
+    // The host link is saturated with about 128K 16-byte loads in flight over the whole chip; more than that
+    // only queues and costs throughput, so the host sizes (copy_threads, copy_unroll) per request.
+    const int total = m * row16, nt = a.copy_threads;
+    if (tid < nt) {
+      if (a.copy_unroll == 1) copy_missed_rows<1>(hostr, hotr, mtok, vict, total, row16, tid, nt);
+      else if (a.copy_unroll == 2) copy_missed_rows<2>(hostr, hotr, mtok, vict, total, row16, tid, nt);
+      else copy_missed_rows<4>(hostr, hotr, mtok, vict, total, row16, tid, nt);
     }
   } else {
     const int total = k * row16;
@@ -514,7 +529,7 @@ __global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
 }
 
 // Rows of a plan: workgroup (g, r) copies every gridDim.x-th group of 16-byte chunks of request r's
-// missed rows from the pinned host pool into their victim slots.
+// missed rows from the pinned host pool into their victim slots, one load in flight per thread.
 __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
   const int r = blockIdx.y;
   const int m = a.miss[r];
@@ -527,25 +542,11 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
   const v4u* hostr = a.host + (size_t)r * a.H * row16;
   v4u* hotr = a.hot + (size_t)r * a.B * row16;
   const int stride = gridDim.x * blockDim.x;
-  for (int c0 = blockIdx.x * blockDim.x + threadIdx.x; c0 < total; c0 += stride * kUnroll) {
-    v4u v[kUnroll];
-    long long dst[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = c0 + u * stride;
-      dst[u] = -1;
-      if (c < total) {
-        const int j = c / row16, q = c - j * row16;
-        const int x = ptok[j], s = pslot[j];
-        if (x >= 0 && x < a.H && s >= 0 && s < a.B) {
-          v[u] = load_host(hostr + (size_t)x * row16 + q);
-          dst[u] = (long long)s * row16 + q;
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (dst[u] >= 0) hotr[dst[u]] = v[u];
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
+    const int j = c / row16, q = c - j * row16;
+    const int x = ptok[j], s = pslot[j];
+    if (x >= 0 && x < a.H && s >= 0 && s < a.B)
+      hotr[(size_t)s * row16 + q] = load_host(hostr + (size_t)x * row16 + q);
   }
 }
 
@@ -610,6 +611,44 @@ hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Offload: n device rows of request r become host-pool rows pos[r] .. pos[r] + n - 1 (16-byte stores over
+// the host link into the mapped pool); a row whose token sits in a hot slot is written there too, so the
+// slot keeps holding its token's row. Rows that would fall outside [0, H) are skipped and reported.
+__global__ __launch_bounds__(256) void offload_kernel(OffloadArgs a) {
+  const int r = blockIdx.y;
+  const int row16 = a.row16, n = a.n;
+  const int p0 = a.pos[r];
+  const int total = n * row16;
+  const size_t rH = (size_t)r * a.H, rB = (size_t)r * a.B;
+  const v4u* src = a.rows + (size_t)r * n * row16;
+  v4u* hostr = a.host + rH * row16;
+  v4u* hotr = a.hot + rB * row16;
+  bool skipped = false;
+  const int stride = gridDim.x * blockDim.x;
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
+    const int j = c / row16, q = c - j * row16;
+    const int64_t x = (int64_t)p0 + j;
+    if (x < 0 || x >= a.H) {
+      skipped = true;
+      continue;
+    }
+    const v4u v = src[c];
+    __builtin_nontemporal_store(v, hostr + (size_t)x * row16 + q);
+    const int s = a.page[rH + x];
+    if (s >= 0 && s < a.B) hotr[(size_t)s * row16 + q] = v;
+  }
+  if (a.status && skipped) a.status[r] = kStatusBadId;  // same value from every thread that skipped
+}
+
+hipError_t launch_offload(const OffloadArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  const int64_t chunks = (int64_t)a.n * a.row16;
+  int g = (int)((chunks + 255) / 256);
+  if (g > 64) g = 64;
+  hipLaunchKernelGGL(offload_kernel, dim3(g, a.R), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 // Rebuilds request r's LRU order list from its stamps: the rank of slot s is the number of slots with a
 // smaller (stamp, slot) key, counted against all B stamps staged in LDS. Used after a caller imports
 // tables that did not carry the order list; O(B^2 / 1024) per thread, off the decode path.
@@ -637,33 +676,40 @@ hipError_t launch_rebuild_order(const RebuildArgs& a, hipStream_t s) {
 }
 
 hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes) {
-  hipError_t e = hipFuncSetAttribute((const void*)resolve_kernel<kFused>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)resolve_bytes);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)resolve_kernel<kPlan>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)resolve_bytes);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)resolve_kernel<kTrial>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)resolve_bytes);
-  if (e != hipSuccess) return e;
+  const void* resolve_variants[] = {
+      (const void*)resolve_kernel<kFused, false>, (const void*)resolve_kernel<kFused, true>,
+      (const void*)resolve_kernel<kPlan, false>,  (const void*)resolve_kernel<kPlan, true>,
+      (const void*)resolve_kernel<kTrial, false>, (const void*)resolve_kernel<kTrial, true>,
+  };
+  hipError_t e = hipSuccess;
+  for (const void* f : resolve_variants) {
+    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)resolve_bytes);
+    if (e != hipSuccess) return e;
+  }
   e = hipFuncSetAttribute((const void*)commit_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)rebuild_bytes);
   if (e != hipSuccess) return e;
   return hipFuncSetAttribute((const void*)rebuild_order_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                              (int)rebuild_bytes);
 }
 
+template <int kMode>
+static void launch_mode(const ResolveArgs& a, hipStream_t s) {
+  if (a.policy == 1) hipLaunchKernelGGL((resolve_kernel<kMode, true>), dim3(a.R), dim3(kThreads), a.L.total, s, a);
+  else hipLaunchKernelGGL((resolve_kernel<kMode, false>), dim3(a.R), dim3(kThreads), a.L.total, s, a);
+}
+
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {
-  if (a.trial) hipLaunchKernelGGL(resolve_kernel<kTrial>, dim3(a.R), dim3(kThreads), a.L.total, s, a);
-  else if (a.plan) hipLaunchKernelGGL(resolve_kernel<kPlan>, dim3(a.R), dim3(kThreads), a.L.total, s, a);
-  else hipLaunchKernelGGL(resolve_kernel<kFused>, dim3(a.R), dim3(kThreads), a.L.total, s, a);
+  if (a.trial) launch_mode<kTrial>(a, s);
+  else if (a.plan) launch_mode<kPlan>(a, s);
+  else launch_mode<kFused>(a, s);
   return hipGetLastError();
 }
 
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
-  // about 2048 workgroups over the whole chip whatever the number of requests
-  int g = (2048 + a.R - 1) / a.R;
+  // about 128K threads (one 16-byte host load in flight each) over the whole chip
+  int g = (512 + a.R - 1) / a.R;
   if (g < 1) g = 1;
-  if (g > 64) g = 64;
+  if (g > 512) g = 512;
   hipLaunchKernelGGL(copy_kernel, dim3(g, a.R), dim3(256), 0, s, a);
   return hipGetLastError();
 }

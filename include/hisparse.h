@@ -189,6 +189,20 @@ int hs_trial(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t
 int hs_commit(hs_ctx* ctx, const int32_t* d_trial, const void* d_gather, const int32_t* d_accept, int32_t* d_status,
               void* stream);
 
+/*
+ * Offload of device rows to the host pool: HiSparse keeps inactive KV in host memory and only a hot buffer
+ * on the GPU (「HiSparse：階層化メモリシステムによるスパースアテンションの加速」, section 「HiSparseの設計」;
+ * "HiSparse: Turbocharging Sparse Attention with Hierarchical Memory", section 2), and the vLLM variant
+ * copies finished prefix pages to host memory ahead of eviction ("vLLM GLM 5.3 最適化: Hybrid HiSparse
+ * オフローディング", section 1 Full Residency).
+ * For every request r, the n rows d_rows[r][0..n) ([R][n][row_bytes], device, 16-byte aligned) become host
+ * rows d_pos[r] .. d_pos[r] + n - 1 of its pool, written by the GPU over the host link. When such a token
+ * currently sits in a hot slot, the slot's row is replaced too, so every slot keeps holding its token's
+ * row. Rows that would fall outside [0, host_rows) are skipped and set HS_STATUS_BAD_ID in d_status[r]
+ * (optional; not written otherwise). Stream-ordered with resolves: a later resolve fetches the new rows.
+ */
+int hs_offload(hs_ctx* ctx, const void* d_rows, const int32_t* d_pos, int32_t n, int32_t* d_status, void* stream);
+
 /* Unfused gather: d_gather[r][i] = the row d_out[r][i] names (as in hs_resolve), zeros for -1 or for
  * an index outside [0, B + T). d_out [R][k] int32, d_gather [R][k][row_bytes]. */
 int hs_gather(hs_ctx* ctx, const int32_t* d_out, void* d_gather, void* stream);

@@ -54,6 +54,8 @@ def load(path: Optional[str] = None):
     lib.oracle_reset.restype = None
     lib.oracle_resolve_batch.argtypes = [ctypes.POINTER(Dims), ctypes.c_int32] + [vp] * 13
     lib.oracle_resolve_batch.restype = ctypes.c_int
+    lib.oracle_offload.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32]
+    lib.oracle_offload.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -109,3 +111,14 @@ class Oracle:
         if rc != 0:
             raise RuntimeError(f"oracle step failed ({rc}): more misses than free slots")
         return out, miss, status, g
+
+    def offload(self, rows: np.ndarray, pos: np.ndarray) -> np.ndarray:
+        """rows: uint8 [n_req, n, row_bytes] written as host rows pos[r] .. pos[r] + n - 1 (and into the hot slot
+        of a token that has one). Returns the per-request status."""
+        rows = np.ascontiguousarray(rows, dtype=np.uint8)
+        n = rows.shape[1]
+        st = np.zeros(self.n, np.int32)
+        for r in range(self.n):
+            st[r] = self.lib.oracle_offload(ctypes.byref(self.dims), _p(self.host[r]), _p(self.hot[r]),
+                                            _p(self.page[r]), _p(rows[r]), int(pos[r]), n)
+        return st

@@ -185,3 +185,23 @@ int oracle_resolve_batch(const oracle_dims* d, int32_t n, int32_t* slot_tok, int
   }
   return 0;
 }
+
+/*
+ * Offload of device rows into one request's host pool: row j becomes host row pos + j, and a slot that
+ * holds that token gets the same row (inactive KV lives in host memory, "HiSparse: Turbocharging Sparse
+ * Attention with Hierarchical Memory", section 2; finished prefix pages are copied to host memory ahead of
+ * eviction, "vLLM GLM 5.3 最適化: Hybrid HiSparse オフローディング", section 1 Full Residency). Rows outside
+ * [0, H) are skipped; returns ORACLE_BAD_ID if any was, else 0.
+ */
+int oracle_offload(const oracle_dims* d, uint8_t* host, uint8_t* hot, const int32_t* page, const uint8_t* rows,
+                   int32_t pos, int32_t n) {
+  const int64_t rb = d->row_bytes;
+  int status = 0;
+  for (int32_t j = 0; j < n; ++j) {
+    const int64_t x = (int64_t)pos + j;
+    if (x < 0 || x >= d->H) { status = ORACLE_BAD_ID; continue; }
+    memcpy(host + x * rb, rows + (int64_t)j * rb, (size_t)rb);
+    if (page[x] != -1) memcpy(hot + (int64_t)page[x] * rb, rows + (int64_t)j * rb, (size_t)rb);
+  }
+  return status;
+}

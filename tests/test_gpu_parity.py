@@ -439,3 +439,62 @@ def test_fifo_plan_trial_commit():
         p.t += 1
         p.check_state()
     p.close()
+
+
+def test_offload_rows_then_resolve():
+    """hs_offload writes device rows into the host pool (and into the hot slot of a token that has one);
+    later resolves fetch the new rows. Pool, slots and every later output equal the oracle's."""
+    import hierarchical_memory_amd as hm
+    w = workload.GROW_32.with_(num_requests=6, steps=20)
+    p = Pair(w)
+    R, rb = w.num_requests, w.row_bytes
+    for _ in range(8):
+        p.step()
+    n = 700
+    rows = np.empty((R, n, rb), np.uint8)
+    workload.fill_rows(rows.view(np.uint16).reshape(R * n, rb // 2), 0, R * n, rb // 2, 4242)
+    pos = np.array([0, 5000, 30000, w.host_rows - 300, 32000, 12345], np.int32)
+    status = torch.zeros((R,), dtype=torch.int32, device="cuda")
+    hm.hs_offload(p.sw.ctx, torch.from_numpy(rows).cuda(), torch.from_numpy(pos).cuda(), status)
+    o_st = p.o.offload(rows, pos)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == o_st).all() and o_st[3] == hm.HS_STATUS_BAD_ID
+    pool = p.sw.host_pool()
+    for r in range(R):
+        a = int(pos[r])
+        b = min(w.host_rows, a + n)
+        assert (pool[r][a:b] == p.o.host[r][a:b]).all() and (pool[r][a:b] == rows[r][:b - a]).all()
+    p.check_state()
+    for _ in range(8, w.steps):
+        p.step(check_state=True)
+    p.close()
+
+
+def test_large_topk_equal_buffer():
+    """k = B = 4096 (the largest top-k whose workgroup fits the LDS with this context): every free slot is a
+    victim each step."""
+    w = workload.SINGLE_4K.with_(name="k4096", num_requests=3, top_k=4096, buffer_slots=4096, host_rows=16384,
+                                 L0=16384, window=8192, steps=10)
+    p = Pair(w)
+    p.run(check_every=2)
+    p.close()
+
+
+def test_many_small_requests():
+    """1500 requests (1500 workgroups, more than the 256 CUs), tiny k and B."""
+    rng = np.random.default_rng(8)
+    w = workload.SINGLE_4K.with_(name="many", num_requests=1500, top_k=8, buffer_slots=8, host_rows=64, L0=64,
+                                 steps=6, row_elems=8)
+    ids = _random_ids(rng, 1500, 6, 8, 64, p_weird=0.05)
+    p = Pair(w, ids=ids, sample=[0, 1, 777, 1499])
+    p.run(check_every=1)
+    p.check_all_requests(rows_per_request=4)
+    p.close()
+
+
+def test_whole_set_kept():
+    """keep = 100 %: k misses at step 0, none after; slots and rows never move."""
+    p = Pair(workload.SINGLE_4K.with_(keep_permille=1000))
+    p.run(check_every=4)
+    assert int(p.outs[1][0].item()) == 0
+    p.close()

@@ -391,3 +391,32 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     mut.write_text(src.replace(old, new))
     lib = oracle.build(force=True, src=str(mut), dst=str(tmp_path / "libmutant.so"))
     assert not _run_pins_against(lib), f"no pin caught: {name}"
+
+
+def test_offload_keeps_slots_consistent():
+    """Offloaded rows replace host rows, and the hot row of a token that sits in a slot; rows outside the pool
+    are skipped with the bad-id bit. Afterwards every slot still holds its token's host row and a gather
+    returns the new rows."""
+    w = workload.SINGLE_4K.with_(num_requests=2, steps=12)
+    ids = workload.streams(w)
+    host = make_host(2, w.host_rows, 32)
+    o = oracle.Oracle(2, w.buffer_slots, w.top_k, w.host_rows, 32, host=host)
+    for t in range(6):
+        o.step(ids[:, t])
+    n = 300
+    rows = np.empty((2, n, 32), np.uint8)
+    workload.fill_rows(rows.view(np.uint16).reshape(2 * n, 16), 0, 2 * n, 16, 99)
+    pos = np.array([w.host_rows - 200, 1000], np.int32)  # request 0 runs past the end of its pool
+    in_slots = [int((o.page[1][1000:1300] >= 0).sum())]
+    assert in_slots[0] > 0
+    st = o.offload(rows, pos)
+    assert st.tolist() == [oracle.BAD_ID, 0]
+    assert (o.host[0][w.host_rows - 200:] == rows[0][:200]).all()
+    assert (o.host[1][1000:1300] == rows[1]).all()
+    for r in range(2):
+        occ = np.nonzero(o.slot_tok[r] >= 0)[0]
+        assert (o.hot[r][occ] == o.host[r][o.slot_tok[r][occ]]).all()
+    for t in range(6, 12):
+        out, miss, status, g = o.step(ids[:, t], gather=True)
+        for r in range(2):
+            check_invariants(o, r, ids[r, t].tolist(), out[r].tolist(), miss[r], status[r], None, g[r])
