@@ -178,7 +178,7 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step):
     return {"kernel": "resolve_kernel<plan> (hs_plan)", "bound": "hbm", "achieved": hit_gbps, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": hit_gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": meta,
             "avg_launch_us": plan_avg * 1e3, "p50_launch_us": float(np.median(plan_ms)) * 1e3,
-            "traffic": measured_traffic(w.name, "resolve_kernel<true>"),
+            "traffic": measured_traffic(w.name, "resolve_plan"),
             "copy_kernel_avg_us": float(copy_ms.mean()) * 1e3, "copy_kernel_GBps": copy_gbps,
             "split_step_ms": total_ms / K, "same_misses_as_fused": bool(abs(mean_m - mean_miss_per_step) < 1e-6)}
 
@@ -388,7 +388,7 @@ def main() -> int:
         "measured_hbm_copy_GBps": hbm_copy,
         "step_ms_p10_p50_p90": [float(np.percentile(per, q)) for q in (10, 50, 90)],
         "roofline": {"bound": "host_link", "achieved": miss_gbps, "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-                     "frac": miss_gbps / PCIE5_X16_GBPS, "traffic": measured_traffic(w.name, "resolve_kernel<false>"),
+                     "frac": miss_gbps / PCIE5_X16_GBPS, "traffic": measured_traffic(w.name, "resolve_fused"),
                      "kernel": "resolve_kernel",
                      "algorithmic_bytes_per_launch": miss_bytes / K},
         "hbm": {"achieved": hbm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hbm_gbps / HBM_PEAK_GBPS,
