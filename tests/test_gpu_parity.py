@@ -498,3 +498,39 @@ def test_whole_set_kept():
     p.run(check_every=4)
     assert int(p.outs[1][0].item()) == 0
     p.close()
+
+
+def test_graph_replay_plan_copy_and_trial_commit():
+    """The split step (plan + copy) and the retryable step (trial + commit) captured in HIP graphs: every
+    replay, with eager work and synchronisation between replays, equals the oracle."""
+    import hierarchical_memory_amd as hm
+    w = workload.GROW_32.with_(num_requests=4, steps=12)
+    for kind in ("split", "trial"):
+        p = Pair(w, gather=True)
+        topk = torch.empty((w.num_requests, w.top_k), dtype=torch.int32, device="cuda")
+        out, miss, status, g = p.outs
+        plan, trial = p.sw.plan_buffer(), p.sw.trial_buffer()
+        cstat = torch.zeros((w.num_requests,), dtype=torch.int32, device="cuda")
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg, stream=s):
+            if kind == "split":
+                hm.hs_plan(p.sw.ctx, topk, None, out, miss, status, plan)
+                hm.hs_copy(p.sw.ctx, plan, miss)
+            else:
+                hm.hs_trial(p.sw.ctx, topk, None, out, miss, status, g, trial)
+                hm.hs_commit(p.sw.ctx, trial, g, None, cstat)
+        torch.cuda.synchronize()
+        for t in range(w.steps):
+            ids = np.ascontiguousarray(p.ids[:, t])
+            topk.copy_(torch.from_numpy(ids))
+            cg.replay()
+            torch.cuda.synchronize()
+            o_out, o_miss, _, o_g = p.o.step(ids, gather=True)
+            assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all(), (kind, t)
+            if kind == "trial":
+                assert (g.cpu().numpy() == o_g).all() and (cstat.cpu().numpy() == 0).all()
+            p.t += 1
+            p.check_state()
+        p.close()
