@@ -121,7 +121,9 @@ def cpu_baseline(w, ids, seconds: float, policy: int = 0):
                            w.row_elems, w.row_seed)
     tail = tail0 = None
     if w.tail_tokens:
-        tail = np.ascontiguousarray(host[:, w.tail0:w.tail0 + w.tail_tokens])
+        tail = np.zeros((n_req, w.tail_tokens, w.row_bytes), np.uint8)
+        for x in range(w.tail0, w.tail0 + w.tail_tokens):  # the device tail is a ring: token x in row x mod T
+            tail[:, x % w.tail_tokens] = host[:, x]
         tail0 = np.full(n_req, w.tail0, np.int32)
     o = oracle.Oracle(n_req, w.buffer_slots, w.top_k, w.host_rows, w.row_bytes, T=w.tail_tokens, host=host, tail=tail,
                       policy=policy)
@@ -316,7 +318,11 @@ def main() -> int:
     tail0 = None
     if T:
         pool = sw.host_pool()
-        sw.tail.copy_(torch.from_numpy(np.ascontiguousarray(pool[:, w.tail0:w.tail0 + T])))
+        # the device tail is a ring of T rows: token x of the window [tail0, tail0 + T) in row x mod T
+        ring = (np.arange(w.tail0, w.tail0 + T) % T)
+        tail_rows = np.empty((R, T, rb), np.uint8)
+        tail_rows[:, ring] = pool[:, w.tail0:w.tail0 + T]
+        sw.tail.copy_(torch.from_numpy(tail_rows))
         tail0 = torch.full((R,), w.tail0, dtype=torch.int32, device="cuda")
     ids = workload.streams(w, n_steps=n_steps)                      # [R, steps, k]
     topk = torch.from_numpy(np.ascontiguousarray(ids.transpose(1, 0, 2))).cuda()  # [steps, R, k] in HBM

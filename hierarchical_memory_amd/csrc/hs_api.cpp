@@ -403,6 +403,29 @@ int hs_offload(hs_ctx* ctx, const void* d_rows, const int32_t* d_pos, int32_t n,
   return ok();
 }
 
+int hs_advance_tail(hs_ctx* ctx, int32_t* d_tail0, const int32_t* d_n, int32_t* d_status, void* stream) {
+  int rc = check_ready(ctx);
+  if (rc) return rc;
+  if (ctx->cfg.tail_tokens == 0) return fail(HS_E_INVALID, "the context has no device tail (tail_tokens = 0)");
+  if (!d_tail0 || !d_n) return fail(HS_E_INVALID, "tail0 and n must not be NULL");
+  hs::AdvanceTailArgs a{};
+  a.R = ctx->cfg.num_requests;
+  a.B = ctx->cfg.device_buffer_size;
+  a.H = ctx->H;
+  a.T = ctx->cfg.tail_tokens;
+  a.row16 = ctx->cfg.row_bytes / 16;
+  a.tail0 = d_tail0;
+  a.n = d_n;
+  a.status = d_status;
+  a.tail = (const hs::v4u*)ctx->views.tail;
+  a.host = (hs::v4u*)ctx->pool_dev;
+  a.hot = (hs::v4u*)ctx->views.hot;
+  a.page = ctx->views.page;
+  hipError_t e = hs::launch_advance_tail(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "advance-tail launch");
+  return ok();
+}
+
 int hs_rebuild_order(hs_ctx* ctx, void* stream) {
   int rc = check_ready(ctx);
   if (rc) return rc;

@@ -114,6 +114,17 @@ struct OffloadArgs {
   const int32_t* page;
 };
 
+struct AdvanceTailArgs {
+  int32_t R, B, H, T, row16;
+  int32_t* tail0;      // [R], advanced in place
+  const int32_t* n;    // [R]
+  int32_t* status;     // [R] or nullptr
+  const v4u* tail;     // [R][T][row16] ring
+  v4u* host;
+  v4u* hot;
+  const int32_t* page;
+};
+
 struct RebuildArgs {
   int32_t R, B;
   const int32_t* stamp;
@@ -145,6 +156,7 @@ hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_rebuild_order(const RebuildArgs& a, hipStream_t s);
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s);
 hipError_t launch_offload(const OffloadArgs& a, hipStream_t s);
+hipError_t launch_advance_tail(const AdvanceTailArgs& a, hipStream_t s);
 hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes);
 
 }  // namespace hs

@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       o = pos_slot[i];
       g = o;
     } else if (c == C_RES) {
-      o = B + (x - t0);
+      o = B + x % T;  // the tail is a ring: token x in row x mod T
       g = o;
     }
     a.out[rk + i] = o;
@@ -646,6 +646,45 @@ hipError_t launch_offload(const OffloadArgs& a, hipStream_t s) {
   int g = (int)((chunks + 255) / 256);
   if (g > 64) g = 64;
   hipLaunchKernelGGL(offload_kernel, dim3(g, a.R), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// Advances request r's device tail window by n[r] tokens (clamped to [0, T]): the leaving tokens
+// tail0 .. tail0+n-1 have their ring rows (x mod T) written to their host-pool rows over the host link, and
+// to their hot slot if they have one; then tail0 moves. One workgroup per request, so tail0 is updated in
+// place after every thread has read it.
+__global__ __launch_bounds__(1024) void advance_tail_kernel(AdvanceTailArgs a) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int T = a.T, row16 = a.row16;
+  const int32_t t0 = a.tail0[r];
+  int n = a.n[r];
+  n = n < 0 ? 0 : n > T ? T : n;
+  const size_t rH = (size_t)r * a.H, rB = (size_t)r * a.B;
+  const v4u* tailr = a.tail + (size_t)r * T * row16;
+  v4u* hostr = a.host + rH * row16;
+  v4u* hotr = a.hot + rB * row16;
+  int skipped = 0;
+  for (int c = tid; c < n * row16; c += blockDim.x) {
+    const int j = c / row16, q = c - j * row16;
+    const int64_t x = (int64_t)t0 + j;
+    if (x < 0 || x >= a.H) {
+      skipped = 1;
+      continue;
+    }
+    const v4u v = tailr[(size_t)(x % T) * row16 + q];
+    __builtin_nontemporal_store(v, hostr + (size_t)x * row16 + q);
+    const int s = a.page[rH + x];
+    if (s >= 0 && s < a.B) hotr[(size_t)s * row16 + q] = v;
+  }
+  skipped = __syncthreads_or(skipped);
+  if (tid == 0) {
+    a.tail0[r] = t0 + n;
+    if (a.status) a.status[r] = skipped ? kStatusBadId : 0;
+  }
+}
+
+hipError_t launch_advance_tail(const AdvanceTailArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(advance_tail_kernel, dim3(a.R), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

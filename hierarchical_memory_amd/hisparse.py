@@ -21,8 +21,8 @@ HS_STATUS_BAD_ID, HS_STATUS_DUP_ID, HS_STATUS_BAD_STATE, HS_STATUS_STALE = 1, 2,
 HS_EVICT_LRU, HS_EVICT_FIFO = 0, 1
 
 EXPORTED = ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
-            "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_offload", "hs_gather", "hs_rebuild_order",
-            "hs_destroy", "hs_last_error")
+            "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_offload", "hs_advance_tail", "hs_gather",
+            "hs_rebuild_order", "hs_destroy", "hs_last_error")
 
 
 class HiSparseError(RuntimeError):
@@ -77,6 +77,7 @@ def lib():
         L.hs_trial.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.hs_commit.argtypes = [vp, vp, vp, vp, vp, vp]
         L.hs_offload.argtypes = [vp, vp, vp, i32, vp, vp]
+        L.hs_advance_tail.argtypes = [vp, vp, vp, vp, vp]
         L.hs_gather.argtypes = [vp, vp, vp, vp]
         L.hs_rebuild_order.argtypes = [vp, vp]
         L.hs_destroy.argtypes = [vp]
@@ -84,7 +85,8 @@ def lib():
         L.hs_last_error.argtypes = []
         L.hs_last_error.restype = ctypes.c_char_p
         for name in ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
-                     "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_offload", "hs_gather", "hs_rebuild_order"):
+                     "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_offload", "hs_advance_tail", "hs_gather",
+                     "hs_rebuild_order"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -194,6 +196,11 @@ def hs_offload(ctx, rows, pos, status=None, stream=None) -> None:
     """rows: device uint8 [R, n, row_bytes]; pos: device int32 [R]."""
     _check(lib().hs_offload(ctx, _ptr(rows), _ptr(pos), int(rows.shape[1]) if rows is not None else 0,
                             _ptr(status), _stream(stream)))
+
+
+def hs_advance_tail(ctx, tail0, n, status=None, stream=None) -> None:
+    """tail0: device int32 [R], advanced in place; n: device int32 [R]."""
+    _check(lib().hs_advance_tail(ctx, _ptr(tail0), _ptr(n), _ptr(status), _stream(stream)))
 
 
 def hs_gather(ctx, out, gather, stream=None) -> None:

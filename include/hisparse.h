@@ -96,7 +96,8 @@ typedef struct hs_config {
  */
 typedef struct hs_device_views {
   void* hot;            uint64_t hot_bytes;       /* [R][B][row_bytes] hot buffer rows */
-  void* tail;           uint64_t tail_bytes;      /* [R][T][row_bytes] resident tail rows; NULL when T == 0 */
+  void* tail;           uint64_t tail_bytes;      /* [R][T][row_bytes] resident tail ring (token x in row
+                                                     x mod T); NULL when T == 0 */
   int32_t* slot_tok;    uint64_t slot_tok_bytes;  /* [R][B] token held by each slot, -1 = empty */
   int32_t* stamp;       uint64_t stamp_bytes;     /* [R][B] last-use step of each slot, -1 = empty */
   uint16_t* lru_order;  uint64_t lru_order_bytes; /* [R][B] slots in ascending (stamp, slot) (library-maintained) */
@@ -141,8 +142,9 @@ int hs_reset(hs_ctx* ctx, const int32_t* d_request_ids, int32_t n, void* stream)
  * One decode step for every request (one workgroup per request).
  *   d_topk    [R][k] int32: selected token ids; -1 = padding.
  *   d_tail0   [R] int32 or NULL: first device-resident token of each request; a token x with
- *             tail0 <= x < tail0 + T resolves to B + (x - tail0) and takes no slot.
- *   d_out     [R][k] int32: slot of each id (hit or newly filled), B + tail index for a resident id,
+ *             tail0 <= x < tail0 + T resolves to B + (x mod T) and takes no slot. The device tail is a
+ *             ring of T rows per request: token x of the window [tail0, tail0 + T) is in row x mod T.
+ *   d_out     [R][k] int32: slot of each id (hit or newly filled), B + tail row for a resident id,
  *             -1 for padding or a bad id.
  *   d_miss    [R] int32: misses (rows fetched from the host pool) of each request.
  *   d_status  [R] int32: HS_STATUS_* bits of this step.
@@ -202,6 +204,18 @@ int hs_commit(hs_ctx* ctx, const int32_t* d_trial, const void* d_gather, const i
  * (optional; not written otherwise). Stream-ordered with resolves: a later resolve fetches the new rows.
  */
 int hs_offload(hs_ctx* ctx, const void* d_rows, const int32_t* d_pos, int32_t n, int32_t* d_status, void* stream);
+
+/*
+ * Tail migration (Mixed residency: under memory pressure the older part of a request's device tail moves
+ * to host memory, "vLLM GLM 5.3 最適化: Hybrid HiSparse オフローディング", section 2). For every request r,
+ * the n = clamp(d_n[r], 0, T) tokens d_tail0[r] .. d_tail0[r] + n - 1 leave the tail: their ring rows are
+ * written to their host-pool rows over the host link (and to the hot slot of a token that has one), then
+ * d_tail0[r] advances by n, in place. Those tokens then resolve through the hot buffer; the ring rows they
+ * free belong to the tokens entering the window at its end, which the caller writes. d_status[r]
+ * (optional) gets HS_STATUS_BAD_ID if a leaving token lies outside [0, host_rows) (its row is skipped),
+ * else 0. Requires tail_tokens > 0.
+ */
+int hs_advance_tail(hs_ctx* ctx, int32_t* d_tail0, const int32_t* d_n, int32_t* d_status, void* stream);
 
 /* Unfused gather: d_gather[r][i] = the row d_out[r][i] names (as in hs_resolve), zeros for -1 or for
  * an index outside [0, B + T). d_out [R][k] int32, d_gather [R][k][row_bytes]. */

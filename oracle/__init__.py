@@ -56,6 +56,8 @@ def load(path: Optional[str] = None):
     lib.oracle_resolve_batch.restype = ctypes.c_int
     lib.oracle_offload.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32]
     lib.oracle_offload.restype = ctypes.c_int
+    lib.oracle_advance_tail.argtypes = [ctypes.POINTER(Dims), vp, vp, vp, vp, vp, ctypes.c_int32]
+    lib.oracle_advance_tail.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -121,4 +123,15 @@ class Oracle:
         for r in range(self.n):
             st[r] = self.lib.oracle_offload(ctypes.byref(self.dims), _p(self.host[r]), _p(self.hot[r]),
                                             _p(self.page[r]), _p(rows[r]), int(pos[r]), n)
+        return st
+
+    def advance_tail(self, tail0: np.ndarray, n: np.ndarray) -> np.ndarray:
+        """Move each request's tail window forward by n[r] tokens (tail0 updated in place, int32 [n_req]);
+        the leaving rows go to the host rows (and hot slots). Returns the per-request status."""
+        assert self.tail is not None and tail0.dtype == np.int32 and tail0.flags.c_contiguous
+        st = np.zeros(self.n, np.int32)
+        for r in range(self.n):
+            st[r] = self.lib.oracle_advance_tail(ctypes.byref(self.dims), _p(self.host[r]), _p(self.tail[r]),
+                                                 _p(self.hot[r]), _p(self.page[r]),
+                                                 ctypes.c_void_p(tail0.ctypes.data + 4 * r), int(n[r]))
         return st

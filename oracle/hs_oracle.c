@@ -78,7 +78,8 @@ void oracle_reset(const oracle_dims* d, int32_t* slot_tok, int32_t* stamp, int32
  *   host[H*row_bytes]: the request's host pool rows; tail[T*row_bytes]: its device tail rows
  *     (may be NULL when has_tail == 0).
  *   ids[k]: the selected token ids; tail0: first resident token when has_tail != 0.
- *   out[k]: slot for a hit or miss, B + (id - tail0) for a resident id, -1 otherwise.
+ *   out[k]: slot for a hit or miss, B + (id mod T) for a resident id, -1 otherwise. The device tail is a
+ *     ring of T rows: it holds the tokens [tail0, tail0 + T), token x in row x mod T.
  *   gather[k*row_bytes] (optional): the row each output names; zeros for -1.
  * Returns 0, or -1 when a request has more misses than free slots (needs B < k).
  */
@@ -107,7 +108,7 @@ int oracle_resolve(const oracle_dims* d, int32_t* slot_tok, int32_t* stamp, int3
     /* repeats are looked for among valid ids only */
     if (seen[x]) { status |= ORACLE_DUP_ID; continue; }
     seen[x] = 1;
-    if (resident) { out[i] = B + (x - tail0); continue; }
+    if (resident) { out[i] = B + x % T; continue; }
     if (page[x] != -1) {
       out[i] = page[x];
       hit[page[x]] = 1;
@@ -203,5 +204,27 @@ int oracle_offload(const oracle_dims* d, uint8_t* host, uint8_t* hot, const int3
     memcpy(host + x * rb, rows + (int64_t)j * rb, (size_t)rb);
     if (page[x] != -1) memcpy(hot + (int64_t)page[x] * rb, rows + (int64_t)j * rb, (size_t)rb);
   }
+  return status;
+}
+
+/*
+ * Advance one request's device tail by n tokens (the Mixed-residency tail migrating to host memory under
+ * pressure, "vLLM GLM 5.3 最適化: Hybrid HiSparse オフローディング", section 2): tokens tail0 .. tail0+n-1
+ * leave the ring; their rows (ring row x mod T) are written to host rows x, and into the hot slot of a token
+ * that has one. n is clamped to [0, T]; tokens at or past H are skipped (ORACLE_BAD_ID). tail0 advances by n.
+ */
+int oracle_advance_tail(const oracle_dims* d, uint8_t* host, const uint8_t* tail, uint8_t* hot, const int32_t* page,
+                        int32_t* tail0, int32_t n) {
+  const int64_t rb = d->row_bytes;
+  int status = 0;
+  if (n < 0) n = 0;
+  if (n > d->T) n = d->T;
+  for (int32_t j = 0; j < n; ++j) {
+    const int64_t x = (int64_t)*tail0 + j;
+    if (x < 0 || x >= d->H) { status = ORACLE_BAD_ID; continue; }
+    memcpy(host + x * rb, tail + (x % d->T) * rb, (size_t)rb);
+    if (page[x] != -1) memcpy(hot + (int64_t)page[x] * rb, tail + (x % d->T) * rb, (size_t)rb);
+  }
+  *tail0 += n;
   return status;
 }

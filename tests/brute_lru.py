@@ -54,7 +54,7 @@ class ListLRU:
                 continue
             seen.add(x)
             if in_tail:
-                out[i] = self.B + (x - tail0)
+                out[i] = self.B + x % self.T
                 continue
             if x in self.where:
                 out[i] = self.where[x]

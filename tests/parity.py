@@ -21,6 +21,16 @@ def log(msg: str) -> None:
     sys.stdout.flush()
 
 
+def ring_tail(rows: np.ndarray, tail0: int, T: int) -> np.ndarray:
+    """Device tail of one request laid out as the boundary defines it: a ring of T rows holding the tokens
+    [tail0, tail0 + T), token x in row x mod T (rows of tokens past the pool stay zero)."""
+    H, rb = rows.shape
+    tail = np.zeros((T, rb), np.uint8)
+    for x in range(max(0, tail0), min(H, tail0 + T)):
+        tail[x % T] = rows[x]
+    return tail
+
+
 def order_sorted_by_stamp(order: np.ndarray, stamp: np.ndarray) -> bool:
     """The library's LRU order list must list slots by ascending (stamp, slot)."""
     o = order.astype(np.int64)
@@ -52,11 +62,7 @@ class Pair:
             self.tail0 = np.full(self.R, w.tail0, np.int32) if tail0 is None else np.asarray(tail0, np.int32)
             self.tail0_dev = torch.from_numpy(self.tail0).cuda()
             # device tail rows = the host rows [tail0, tail0 + T) of each request (zeros past the pool's end)
-            tail = np.zeros((self.R, self.T, self.rb), np.uint8)
-            for r in range(self.R):
-                a = int(self.tail0[r])
-                n = max(0, min(self.T, self.H - a))
-                tail[r, :n] = pool[r, a:a + n]
+            tail = np.stack([ring_tail(pool[r], int(self.tail0[r]), self.T) for r in range(self.R)])
             self.sw.tail.copy_(torch.from_numpy(tail))
         # the oracle's own rows, from the generator
         n = len(self.sample)
@@ -66,11 +72,9 @@ class Pair:
                                w.row_elems, w.row_seed)
         tail_o = None
         if self.T:
-            tail_o = np.zeros((n, self.T, self.rb), np.uint8)
-            for j, r in enumerate(self.sample):
-                a = int(self.tail0[r])
-                m = max(0, min(self.T, self.H - a))
-                tail_o[j, :m] = host_o[j, a:a + m]
+            tail_o = np.stack([ring_tail(host_o[j], int(self.tail0[r]), self.T) for j, r in enumerate(self.sample)])
+            if not len(self.sample):
+                tail_o = np.zeros((0, self.T, self.rb), np.uint8)
         self.o = oracle.Oracle(n, self.B, self.k, self.H, self.rb, T=self.T, host=host_o, tail=tail_o, policy=policy)
         self.ids = workload.streams(w, n_steps=self.n_steps) if ids is None else np.ascontiguousarray(ids, np.int32)
         self.sample_t = torch.tensor(self.sample, dtype=torch.long, device="cuda")

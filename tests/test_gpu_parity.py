@@ -534,3 +534,38 @@ def test_graph_replay_plan_copy_and_trial_commit():
             p.t += 1
             p.check_state()
         p.close()
+
+
+def test_advance_tail_then_resolve():
+    """The tail window moves forward: the leaving tokens' ring rows (overwritten first with fresh rows, as a
+    model would produce them) go to the host pool, tail0 advances on the device, and those tokens then
+    resolve through the hot buffer — all equal to the oracle."""
+    import hierarchical_memory_amd as hm
+    w = workload.HYBRID_64.with_(num_requests=4, steps=18)
+    p = Pair(w, gather=True)
+    R, T, rb = w.num_requests, w.tail_tokens, w.row_bytes
+    for _ in range(6):
+        p.step()
+    n = np.array([64, 1000, 0, 20000], np.int32)  # the last is clamped to T
+    fresh = np.empty((R, T, rb), np.uint8)
+    workload.fill_rows(fresh.view(np.uint16).reshape(R * T, rb // 2), 0, R * T, rb // 2, 555)
+    p.sw.tail.copy_(torch.from_numpy(fresh))
+    p.o.tail[...] = fresh[p.sample]
+    status = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+    hm.hs_advance_tail(p.sw.ctx, p.tail0_dev, torch.from_numpy(n).cuda(), status)
+    t0_o = np.ascontiguousarray(p.tail0[p.sample])
+    old = t0_o.copy()
+    o_st = p.o.advance_tail(t0_o, n[p.sample])
+    torch.cuda.synchronize()
+    new_t0 = p.tail0_dev.cpu().numpy()
+    assert (new_t0 == old + np.minimum(n, T)).all() and (new_t0[p.sample] == t0_o).all()
+    assert (status.cpu().numpy() == 0).all() and (o_st == 0).all()
+    pool = p.sw.host_pool()
+    for j, r in enumerate(p.sample):
+        for x in range(int(old[j]), int(new_t0[r]), 97):
+            assert (pool[r][x] == fresh[r][x % T]).all() and (p.o.host[j][x] == pool[r][x]).all()
+    p.tail0 = new_t0.astype(np.int32)
+    p.check_state()
+    for _ in range(6, w.steps):
+        p.step(check_state=True)
+    p.close()

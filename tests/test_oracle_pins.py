@@ -64,7 +64,7 @@ def check_invariants(o: oracle.Oracle, r: int, ids, out, miss, status, tail0=Non
             else:
                 assert stamp[v] <= o.t[r] - 1
         elif v >= B:
-            assert tail0 is not None and v == B + x - tail0
+            assert tail0 is not None and v == B + x % o.T
         if gathered is not None:
             if v >= 0:
                 assert (gathered[i] == o.host[r][x]).all()
@@ -279,7 +279,9 @@ def test_invariants_on_workload_streams(w):
     tail0 = None
     if w.tail_tokens:
         tail0 = np.full(n, w.tail0, np.int32)
-        tail = np.ascontiguousarray(host[:, w.tail0:w.tail0 + w.tail_tokens])
+        tail = np.zeros((n, w.tail_tokens, rb), np.uint8)
+        for x in range(w.tail0, w.tail0 + w.tail_tokens):  # ring row x mod T
+            tail[:, x % w.tail_tokens] = host[:, x]
     o = oracle.Oracle(n, w.buffer_slots, w.top_k, w.host_rows, rb, T=w.tail_tokens, host=host, tail=tail)
     last = [dict() for _ in range(n)]
     for t in range(w.steps):
@@ -307,8 +309,8 @@ def test_error_paths():
     assert out[0].tolist() == [0, -1, -1, -1, 1, -1] and miss[0] == 2
     assert status[0] == oracle.BAD_ID | oracle.DUP_ID
     out, miss, status, _ = o.step(np.array([[14, 18, 19, 15, 3, 14]], np.int32), np.array([15], np.int32))
-    # 14 < tail0: a miss; 15..18 resident (T=4); 19 outside the tail window; last 14 repeated
-    assert out[0].tolist() == [2, 8 + 3, -1, 8 + 0, 0, -1] and status[0] == oracle.BAD_ID | oracle.DUP_ID
+    # 14 < tail0: a miss; 15..18 resident (T=4, ring row x mod 4); 19 outside the tail window; last 14 repeated
+    assert out[0].tolist() == [2, 8 + 18 % 4, -1, 8 + 15 % 4, 0, -1] and status[0] == oracle.BAD_ID | oracle.DUP_ID
     o.reset()
     assert (o.slot_tok == -1).all() and (o.stamp == -1).all() and (o.page == -1).all() and o.t[0] == 0
 
@@ -326,7 +328,8 @@ MUTANTS = {
     "victims from the newest end": ("const int32_t v = cand[j].val;", "const int32_t v = cand[c - 1 - j].val;"),
     "duplicate not rejected": ("if (seen[x]) { status |= ORACLE_DUP_ID; continue; }", ""),
     "tail window not checked": ("if (resident && (int64_t)x - (int64_t)tail0 >= (int64_t)T)", "if (0)"),
-    "tail index off by one": ("out[i] = B + (x - tail0);", "out[i] = B + (x - tail0) + 1;"),
+    "tail index off by one": ("out[i] = B + x % T;", "out[i] = B + (x + 1) % T;"),
+    "tail indexed from tail0": ("out[i] = B + x % T;", "out[i] = B + (x - tail0);"),
     "step counter not advanced": ("*t_io = t + 1;", "*t_io = t;"),
     "FIFO refreshes hit stamps": ("if (d->policy == ORACLE_LRU)\n    for", "if (1)\n    for"),
     "LRU leaves hit stamps alone": ("if (d->policy == ORACLE_LRU)\n    for", "if (d->policy == ORACLE_FIFO)\n    for"),
@@ -420,3 +423,34 @@ def test_offload_keeps_slots_consistent():
         out, miss, status, g = o.step(ids[:, t], gather=True)
         for r in range(2):
             check_invariants(o, r, ids[r, t].tolist(), out[r].tolist(), miss[r], status[r], None, g[r])
+
+
+def test_advance_tail_moves_rows_to_host():
+    """Advancing the tail window: the leaving tokens' ring rows become their host rows, tail0 moves, and those
+    tokens then resolve through the hot buffer (a miss fetches the former tail row)."""
+    w = workload.HYBRID_64.with_(num_requests=2, steps=10, L0=3000, host_rows=3000, tail_tokens=400, top_k=64,
+                                 buffer_slots=128)
+    ids = workload.streams(w)
+    rb = 32
+    host = make_host(2, w.host_rows, rb)
+    tail0 = np.full(2, w.tail0, np.int32)
+    tail = np.zeros((2, w.tail_tokens, rb), np.uint8)
+    workload.fill_rows(tail.view(np.uint16).reshape(2 * w.tail_tokens, rb // 2), 0, 2 * w.tail_tokens, rb // 2, 77)
+    o = oracle.Oracle(2, w.buffer_slots, w.top_k, w.host_rows, rb, T=w.tail_tokens, host=host, tail=tail)
+    for t in range(4):
+        o.step(ids[:, t], tail0)
+    old_tail0 = tail0.copy()
+    before = o.tail.copy()
+    st = o.advance_tail(tail0, np.array([50, 500], np.int32))  # the second clamps to T = 400
+    assert st.tolist() == [0, 0]
+    assert tail0.tolist() == [old_tail0[0] + 50, old_tail0[1] + 400]
+    for r, n in ((0, 50), (1, 400)):
+        for x in range(old_tail0[r], old_tail0[r] + n):
+            assert (o.host[r][x] == before[r][x % w.tail_tokens]).all()
+    # a token that just left the tail is now a miss whose row comes from the host (the former tail row)
+    x = int(old_tail0[0])
+    sel = np.array([[x] + list(range(1, w.top_k)), list(range(w.top_k))], np.int32)
+    out, miss, status, g = o.step(sel, tail0, gather=True)
+    assert 0 <= out[0][0] < w.buffer_slots and (g[0][0] == before[0][x % w.tail_tokens]).all()
+    for r in range(2):
+        check_invariants(o, r, sel[r].tolist(), out[r].tolist(), miss[r], status[r], int(tail0[r]), g[r])
