@@ -65,6 +65,8 @@ def parse():
                          "512 steps each; reports the 100-step rolling mean of misses per step and the resolve rate")
     ap.add_argument("--policy", choices=["lru", "fifo", "both"], default="lru",
                     help="eviction policy (--sweep: 'both' runs every (B, keep) under LRU and FIFO)")
+    ap.add_argument("--gather-launches", type=int, default=64,
+                    help="timed launches of hs_gather on the last step's selection (0: skip)")
     ap.add_argument("--trial-steps", type=int, default=256,
                     help="steps of the hs_trial + hs_commit leg after a reset (0: skip)")
     ap.add_argument("--split-steps", type=int, default=-1,
@@ -183,6 +185,36 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step):
             "traffic": measured_traffic(w.name, "resolve_plan"),
             "copy_kernel_avg_us": float(copy_ms.mean()) * 1e3, "copy_kernel_GBps": copy_gbps,
             "split_step_ms": total_ms / K, "same_misses_as_fused": bool(abs(mean_m - mean_miss_per_step) < 1e-6)}
+
+
+def gather_leg(hm, torch, np, sw, out, w, n, hbm_copy):
+    """hs_gather (the unfused gather) of the last step's selection, n launches timed one by one: every selected
+    row is read from its hot slot (or tail row) and written to one [R, k, row] output, so it runs against HBM."""
+    R, k, rb = w.num_requests, w.top_k, w.row_bytes
+    stream = torch.cuda.current_stream()
+    g = torch.empty((R, k, rb), dtype=torch.uint8, device="cuda")
+    for _ in range(4):
+        hm.hs_gather(sw.ctx, out, g, stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    for i in range(n):
+        ev[2 * i].record(stream)
+        hm.hs_gather(sw.ctx, out, g, stream)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)])
+    valid = int((out >= 0).sum().item())
+    # a selected row is read once and written once; an entry with no row writes a zero row
+    algo = valid * 2 * rb + (R * k - valid) * rb
+    avg = float(ms.mean())
+    gbps = algo / (avg / 1e3) / 1e9
+    del g
+    log(f"[bench] gather: {avg * 1e3:.1f} us/launch, {gbps:.0f} GB/s of rows read + written")
+    return {"kernel": "gather_kernel (hs_gather)", "bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": algo,
+            "avg_launch_us": avg * 1e3, "p50_launch_us": float(np.median(ms)) * 1e3, "launches": n,
+            "frac_of_measured_hbm_copy": (gbps / hbm_copy) if hbm_copy else None,
+            "traffic": measured_traffic(w.name, "gather")}
 
 
 def sweep(args) -> int:
@@ -400,6 +432,8 @@ def main() -> int:
         "hbm": {"achieved": hbm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hbm_gbps / HBM_PEAK_GBPS,
                 "algorithmic_bytes_per_launch": hbm_bytes},
     }
+    if args.gather_launches > 0:
+        rep["gather"] = gather_leg(hm, torch, np, sw, out, w, args.gather_launches, hbm_copy)
     if args.split_steps != 0:
         rep["hit_path"] = split_leg(hm, torch, np, sw, topk, tail0, W, K if args.split_steps < 0 else args.split_steps,
                                     w, total_miss / K)

@@ -2,6 +2,7 @@
 #include "hisparse.h"
 #include "hs_internal.h"
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -370,6 +371,7 @@ int hs_gather(hs_ctx* ctx, const int32_t* d_out, void* d_gather, void* stream) {
   a.B = ctx->cfg.device_buffer_size;
   a.T = ctx->cfg.tail_tokens;
   a.row16 = ctx->cfg.row_bytes / 16;
+  a.rows = std::max(1, hs::kGatherChunks / a.row16);
   a.out = d_out;
   a.hot = (const hs::v4u*)ctx->views.hot;
   a.tail = (const hs::v4u*)ctx->views.tail;

@@ -141,8 +141,15 @@ struct ResetArgs {
   int32_t* step;
 };
 
+// gather_kernel: threads per workgroup, 16-byte loads in flight per thread, and the chunks one workgroup
+// covers (its row count is the largest that fits, at least one)
+constexpr int kGatherThreads = 256;
+constexpr int kGatherUnroll = 3;
+constexpr int kGatherChunks = kGatherThreads * kGatherUnroll;
+
 struct GatherArgs {
   int32_t R, k, B, T, row16;
+  int32_t rows;  // selected rows per workgroup
   const int32_t* out;
   const v4u* hot;
   const v4u* tail;

@@ -513,18 +513,41 @@ __global__ __launch_bounds__(1024) void reset_kernel(ResetArgs a) {
   if (threadIdx.x == 0) a.step[r] = 0;
 }
 
-__global__ __launch_bounds__(256) void gather_kernel(GatherArgs a) {
-  const size_t total = (size_t)a.R * a.k * a.row16;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
-    const size_t ri = c / (size_t)a.row16;
-    const int q = (int)(c - ri * (size_t)a.row16);
-    const int r = (int)(ri / (size_t)a.k);
-    const int o = a.out[ri];
-    v4u v = {0u, 0u, 0u, 0u};
-    if (o >= 0 && o < a.B) v = a.hot[((size_t)r * a.B + o) * a.row16 + q];
-    else if (o >= a.B && o - a.B < a.T) v = a.tail[((size_t)r * a.T + (o - a.B)) * a.row16 + q];
-    a.gather[c] = v;
+// Workgroup (b, r) gathers rows [b*rows, b*rows + rows) of request r's selection into one contiguous
+// stretch of the output: every thread first loads its kGatherUnroll chunks (16 bytes each; the slot or tail
+// index of each comes from the output array), then stores them non-temporally, so each wave keeps several
+// HBM reads in flight and the output is written once, in order. Entries with no row (-1) give zeros.
+__global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
+  const int r = blockIdx.y;
+  const int i0 = blockIdx.x * a.rows;
+  const int row16 = a.row16;
+  const int n = min(a.rows, a.k - i0) * row16;
+  const int32_t* outr = a.out + (size_t)r * a.k + i0;
+  const v4u* hotr = a.hot + (size_t)r * a.B * row16;
+  const v4u* tailr = a.tail ? a.tail + (size_t)r * a.T * row16 : nullptr;
+  v4u* gr = a.gather + ((size_t)r * a.k + i0) * row16;
+  for (int c0 = threadIdx.x; c0 < n; c0 += kGatherThreads * kGatherUnroll) {
+    int o[kGatherUnroll], q[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int c = c0 + u * kGatherThreads;
+      const int i = (int)((unsigned)c / (unsigned)row16);
+      q[u] = c - i * row16;
+      o[u] = c < n ? outr[i] : -1;
+    }
+    v4u v[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      v[u] = v4u{0u, 0u, 0u, 0u};
+      if (o[u] >= 0 && o[u] < a.B) v[u] = __builtin_nontemporal_load(hotr + (size_t)o[u] * row16 + q[u]);
+      else if (o[u] >= a.B && o[u] - a.B < a.T)
+        v[u] = __builtin_nontemporal_load(tailr + (size_t)(o[u] - a.B) * row16 + q[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int c = c0 + u * kGatherThreads;
+      if (c < n) __builtin_nontemporal_store(v[u], gr + c);
+    }
   }
 }
 
@@ -760,11 +783,10 @@ hipError_t launch_reset(const ResetArgs& a, int n_blocks, hipStream_t s) {
 }
 
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s) {
-  const size_t total = (size_t)a.R * a.k * a.row16;
-  if (total == 0) return hipSuccess;
-  size_t blocks = (total + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  if ((size_t)a.R * a.k * a.row16 == 0) return hipSuccess;
+  if (a.rows < 1) return hipErrorInvalidValue;
+  const unsigned bx = (unsigned)((a.k + a.rows - 1) / a.rows);
+  hipLaunchKernelGGL(gather_kernel, dim3(bx, (unsigned)a.R), dim3(kGatherThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -95,6 +95,7 @@ class Pair:
         if self.gather:
             got_g = g[s].cpu().numpy()
             assert (got_g == o_g).all(), self._where("gather", got_g, o_g)
+        self.last_oracle_gather = o_g
         self.t += 1
         if check_state:
             self.check_state()

@@ -106,6 +106,35 @@ def test_unfused_gather_matches_fused():
     p.close()
 
 
+GATHER_CASES = [  # (k, B, H, T, row_bytes); a workgroup of the gather covers max(1, 768 // (row_bytes / 16)) rows
+    (33, 40, 100, 0, 1152),  # 10 rows per workgroup: the last of 4 workgroups holds 3
+    (65, 130, 257, 17, 80),  # 153 rows per workgroup: one partial workgroup; tail rows
+    (5, 8, 20, 3, 16384),  # 1024 chunks per row: one row per workgroup in two passes, the second ragged
+    (2048, 4096, 8192, 0, 1152),
+]
+
+
+@pytest.mark.parametrize("k,B,H,T,rb", GATHER_CASES, ids=[f"k{k}_B{B}_T{T}_rb{rb}" for k, B, H, T, rb in GATHER_CASES])
+def test_unfused_gather_against_oracle(k, B, H, T, rb):
+    """hs_gather after each step equals the oracle's gathered rows (padding, bad and repeated ids included)."""
+    import hierarchical_memory_amd as hm
+    rng = np.random.default_rng(k + rb)
+    R, steps = 4, 5
+    w = workload.SINGLE_4K.with_(name=f"gather_k{k}_rb{rb}", num_requests=R, top_k=k, buffer_slots=B, host_rows=H,
+                                 L0=H, tail_tokens=T, row_elems=rb // 2, steps=steps, fused_gather=True)
+    ids = _random_ids(rng, R, steps, k, H)
+    tail0 = rng.integers(0, H + 1, size=R).astype(np.int32) if T else None
+    p = Pair(w, ids=ids, tail0=tail0, gather=True)
+    g2 = torch.full((R, k, rb), 0xAB, dtype=torch.uint8, device="cuda")
+    for _ in range(steps):
+        p.step()
+        out = p.outs[0]
+        hm.hs_gather(p.sw.ctx, out, g2)
+        got = g2.cpu().numpy()
+        assert (got == p.last_oracle_gather).all(), p._where("unfused gather", got, p.last_oracle_gather)
+    p.close()
+
+
 def test_buffer_equals_topk_and_whole_context():
     """B = k (every free slot shares the previous step's stamp) and B >= context (compulsory misses only)."""
     for B in (256, 4096):
