@@ -67,6 +67,8 @@ def parse():
                     help="eviction policy (--sweep: 'both' runs every (B, keep) under LRU and FIFO)")
     ap.add_argument("--gather-launches", type=int, default=64,
                     help="timed launches of hs_gather on the last step's selection (0: skip)")
+    ap.add_argument("--offload-launches", type=int, default=32,
+                    help="timed launches of hs_offload (and hs_advance_tail on workloads with a device tail); 0: skip")
     ap.add_argument("--trial-steps", type=int, default=256,
                     help="steps of the hs_trial + hs_commit leg after a reset (0: skip)")
     ap.add_argument("--split-steps", type=int, default=-1,
@@ -75,7 +77,8 @@ def parse():
 
 
 def link_and_hbm_probes(torch):
-    """Measured H2D link peak (pinned 1 GiB, hipMemcpyAsync via torch, median of 10) and HBM copy rate."""
+    """Measured host-to-device link peak (pinned 1 GiB, hipMemcpyAsync via torch, median of 10), HBM copy rate
+    (read + write) and device-to-host link rate (the same copy the other way)."""
     n = 1 << 30
     h = torch.empty(n, dtype=torch.uint8, pin_memory=True)
     d = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -96,10 +99,11 @@ def link_and_hbm_probes(torch):
         return ts[len(ts) // 2]
 
     link_ms = med(lambda: d.copy_(h, non_blocking=True))
+    d2h_ms = med(lambda: h.copy_(d, non_blocking=True))
     hbm_ms = med(lambda: d2.copy_(d))
     del h, d, d2
     torch.cuda.empty_cache()
-    return n / link_ms / 1e6, 2 * n / hbm_ms / 1e6
+    return n / link_ms / 1e6, 2 * n / hbm_ms / 1e6, n / d2h_ms / 1e6
 
 
 def cpu_baseline(w, ids, seconds: float, policy: int = 0):
@@ -215,6 +219,65 @@ def gather_leg(hm, torch, np, sw, out, w, n, hbm_copy):
             "avg_launch_us": avg * 1e3, "p50_launch_us": float(np.median(ms)) * 1e3, "launches": n,
             "frac_of_measured_hbm_copy": (gbps / hbm_copy) if hbm_copy else None,
             "traffic": measured_traffic(w.name, "gather")}
+
+
+def _timed_launches(torch, np, n, warm, launch):
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        launch(stream)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    for i in range(n):
+        ev[2 * i].record(stream)
+        launch(stream)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    return np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)])
+
+
+OFFLOAD_ROWS = 64  # rows per request per offload / tail advance
+
+
+def offload_leg(hm, torch, np, sw, w, n, d2h_peak):
+    """hs_offload of OFFLOAD_ROWS device rows per request into the host pool (the residency transition from
+    device to host), n launches timed one by one. It runs last: it rewrites host rows the other legs read."""
+    R, H, rb = w.num_requests, w.host_rows, w.row_bytes
+    rows = torch.full((R, OFFLOAD_ROWS, rb), 7, dtype=torch.uint8, device="cuda")
+    pos = torch.full((R,), H - OFFLOAD_ROWS, dtype=torch.int32, device="cuda")
+    status = torch.zeros(R, dtype=torch.int32, device="cuda")
+    ms = _timed_launches(torch, np, n, 4, lambda st: hm.hs_offload(sw.ctx, rows, pos, status, st))
+    if status.cpu().numpy().any():
+        raise SystemExit("device status bits set during the offload leg")
+    link_bytes = R * OFFLOAD_ROWS * rb
+    avg = float(ms.mean())
+    gbps = link_bytes / (avg / 1e3) / 1e9
+    log(f"[bench] offload: {avg * 1e3:.1f} us/launch, {gbps:.1f} GB/s device to host")
+    return {"kernel": "offload_kernel (hs_offload)", "bound": "host_link", "rows_per_request": OFFLOAD_ROWS,
+            "achieved": gbps, "peak": PCIE5_X16_GBPS, "unit": "GB/s", "frac": gbps / PCIE5_X16_GBPS,
+            "frac_of_measured_d2h": (gbps / d2h_peak) if d2h_peak else None, "link_bytes_per_launch": link_bytes,
+            "avg_launch_us": avg * 1e3, "p50_launch_us": float(np.median(ms)) * 1e3, "launches": n}
+
+
+def advance_tail_leg(hm, torch, np, sw, w, tail0, n, d2h_peak):
+    """hs_advance_tail by OFFLOAD_ROWS tokens per request per launch on a copy of the tail window starts:
+    the leaving tail rows go to the host pool over the link."""
+    R, H, rb = w.num_requests, w.host_rows, w.row_bytes
+    t0 = tail0.clone()
+    if int(t0.max().item()) + (n + 4) * OFFLOAD_ROWS > H:
+        return None
+    step = torch.full((R,), OFFLOAD_ROWS, dtype=torch.int32, device="cuda")
+    status = torch.zeros(R, dtype=torch.int32, device="cuda")
+    ms = _timed_launches(torch, np, n, 4, lambda st: hm.hs_advance_tail(sw.ctx, t0, step, status, st))
+    if status.cpu().numpy().any():
+        raise SystemExit("device status bits set during the tail leg")
+    link_bytes = R * OFFLOAD_ROWS * rb
+    avg = float(ms.mean())
+    gbps = link_bytes / (avg / 1e3) / 1e9
+    log(f"[bench] advance tail: {avg * 1e3:.1f} us/launch, {gbps:.1f} GB/s device to host")
+    return {"kernel": "advance_tail_kernel (hs_advance_tail)", "bound": "host_link", "rows_per_request": OFFLOAD_ROWS,
+            "achieved": gbps, "peak": PCIE5_X16_GBPS, "unit": "GB/s", "frac": gbps / PCIE5_X16_GBPS,
+            "frac_of_measured_d2h": (gbps / d2h_peak) if d2h_peak else None, "link_bytes_per_launch": link_bytes,
+            "avg_launch_us": avg * 1e3, "p50_launch_us": float(np.median(ms)) * 1e3, "launches": n}
 
 
 def sweep(args) -> int:
@@ -337,10 +400,11 @@ def main() -> int:
         raise SystemExit(f"{n_steps} steps outgrow the {H}-row host pool of {w.name}")
     torch.cuda.set_device(0)
 
-    link_peak = hbm_copy = None
+    link_peak = hbm_copy = d2h_peak = None
     if not args.no_probes:
-        link_peak, hbm_copy = link_and_hbm_probes(torch)
-        log(f"[bench] measured H2D link {link_peak:.1f} GB/s, HBM copy {hbm_copy:.0f} GB/s (read+write)")
+        link_peak, hbm_copy, d2h_peak = link_and_hbm_probes(torch)
+        log(f"[bench] measured H2D link {link_peak:.1f} GB/s, D2H link {d2h_peak:.1f} GB/s, "
+            f"HBM copy {hbm_copy:.0f} GB/s (read+write)")
 
     log(f"[bench] {w.name}: R={R} k={k} B={B} host_rows={H} T={T}, warmup {W} + timed {K} steps")
     t0 = time.perf_counter()
@@ -366,9 +430,15 @@ def main() -> int:
     log(f"[bench] setup {time.perf_counter() - t0:.1f} s (pool {R * H * rb / 1e9:.2f} GB pinned)")
 
     stream = torch.cuda.current_stream()
+    cold = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     for t in range(W):
+        if t == 0:
+            cold[0].record(stream)
         hm.hs_resolve(sw.ctx, topk[t], tail0, out, miss[t], status[t], g, stream)
+        if t == 0:
+            cold[1].record(stream)
     torch.cuda.synchronize()
+    cold_ms = cold[0].elapsed_time(cold[1]) if W else None
     log(f"[bench] warmup done")
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     torch.cuda.synchronize()   # one process, one GPU: the barrier is this synchronize
@@ -425,6 +495,9 @@ def main() -> int:
         "miss_copy_frac_of_measured_link": (miss_gbps / link_peak) if link_peak else None,
         "measured_hbm_copy_GBps": hbm_copy,
         "step_ms_p10_p50_p90": [float(np.percentile(per, q)) for q in (10, 50, 90)],
+        "cold_step0_ms": cold_ms,
+        "cold_step0_misses_per_request": float(miss[0].float().mean().item()) if W else None,
+        "measured_d2h_link_GBps": d2h_peak,
         "roofline": {"bound": "host_link", "achieved": miss_gbps, "peak": PCIE5_X16_GBPS, "unit": "GB/s",
                      "frac": miss_gbps / PCIE5_X16_GBPS, "traffic": measured_traffic(w.name, "resolve_fused"),
                      "kernel": "resolve_kernel",
@@ -440,6 +513,10 @@ def main() -> int:
     if args.trial_steps > 0:
         kt = min(args.trial_steps, K)
         rep["trial_commit"] = trial_leg(hm, torch, np, sw, topk, tail0, W, kt, w)
+    if args.offload_launches > 0:
+        rep["offload"] = offload_leg(hm, torch, np, sw, w, args.offload_launches, d2h_peak)
+        if T:
+            rep["advance_tail"] = advance_tail_leg(hm, torch, np, sw, w, tail0, args.offload_launches, d2h_peak)
     sw.close()
     del topk
     if not args.no_cpu_baseline:
