@@ -141,9 +141,48 @@ def cpu_baseline(w, ids, seconds: float, policy: int = 0):
         misses += int(miss.sum())
     dt = time.perf_counter() - t0
     entries = n_req * n_steps * w.top_k
-    return {"value": entries / dt, "unit": "entries/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_req} of {w.num_requests} requests x all {n_steps} steps ({dt:.1f} s, single thread)",
-            "miss_copy_GBps": misses * w.row_bytes / dt / 1e9}
+    rep = {"value": entries / dt, "unit": "entries/s", "cores": 1, "kind": "oracle",
+           "sample": f"{n_req} of {w.num_requests} requests x all {n_steps} steps ({dt:.1f} s, single thread)",
+           "miss_copy_GBps": misses * w.row_bytes / dt / 1e9}
+    rep["all_cores"] = _oracle_all_cores(w, sub, host, tail, tail0, policy, n_steps)
+    return rep
+
+
+def _oracle_all_cores(w, sub, host, tail, tail0, policy, n_steps):
+    """The same oracle on the same sample, its requests split over one thread per available core (at most 16,
+    the host share of one GPU); each thread steps its own requests (the C calls release the GIL)."""
+    import threading
+    import numpy as np
+    import oracle
+    n_req = sub.shape[0]
+    cores = max(1, min(16, len(os.sched_getaffinity(0)), n_req))
+    bounds = np.linspace(0, n_req, cores + 1).astype(int)
+    parts = []
+    for c in range(cores):
+        a, b = int(bounds[c]), int(bounds[c + 1])
+        o = oracle.Oracle(b - a, w.buffer_slots, w.top_k, w.host_rows, w.row_bytes, T=w.tail_tokens, host=host[a:b],
+                          tail=None if tail is None else tail[a:b], policy=policy)
+        parts.append((o, np.ascontiguousarray(sub[a:b]), None if tail0 is None else tail0[a:b]))
+
+    def run(o, ids, t0):
+        for t in range(n_steps):
+            o.step(ids[:, t], t0, gather=w.fused_gather)
+
+    threads = [threading.Thread(target=run, args=part) for part in parts]
+    t_start = time.perf_counter()
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    dt = time.perf_counter() - t_start
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": n_req * n_steps * w.top_k / dt, "unit": "entries/s", "cores": cores, "kind": "oracle",
+            "sample": f"the same {n_req} requests x {n_steps} steps on {cores} threads ({dt:.1f} s)", "cpu_model": model}
 
 
 def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step):
@@ -189,6 +228,51 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step):
             "traffic": measured_traffic(w.name, "resolve_plan"),
             "copy_kernel_avg_us": float(copy_ms.mean()) * 1e3, "copy_kernel_GBps": copy_gbps,
             "split_step_ms": total_ms / K, "same_misses_as_fused": bool(abs(mean_m - mean_miss_per_step) < 1e-6)}
+
+
+def overlap_leg(hm, torch, np, sw, topk, tail0, W, K, w):
+    """The split path pipelined over two streams from a reset: the plan of step t+1 runs on the launch stream
+    while the copy of step t is still in flight on a second stream (plans double-buffered; a plan depends only
+    on the previous plan, whose metadata is final when it ends; copies stay in order on their stream)."""
+    R, k = w.num_requests, w.top_k
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    sw.reset()
+    plans = [sw.plan_buffer() for _ in range(2)]
+    outs = [torch.empty((R, k), dtype=torch.int32, device="cuda") for _ in range(2)]
+    miss = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
+    status = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
+    copied = [None, None]
+
+    def step(t):
+        b = t % 2
+        if copied[b] is not None:
+            main.wait_event(copied[b])  # the copy that read this plan buffer is done
+        hm.hs_plan(sw.ctx, topk[t], tail0, outs[b], miss[t], status[t], plans[b], main)
+        planned = torch.cuda.Event()
+        planned.record(main)
+        side.wait_event(planned)
+        hm.hs_copy(sw.ctx, plans[b], miss[t], side)
+        copied[b] = torch.cuda.Event()
+        copied[b].record(side)
+
+    for t in range(W):
+        step(t)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(main)
+    for t in range(W, W + K):
+        step(t)
+    main.wait_event(copied[(W + K - 1) % 2])
+    end.record(main)
+    torch.cuda.synchronize()
+    if status[W:].cpu().numpy().any():
+        raise SystemExit("device status bits set during the overlap leg")
+    ms = start.elapsed_time(end) / K
+    m = miss[W:].cpu().numpy().astype(np.int64)
+    log(f"[bench] overlapped split: {ms:.3f} ms/step ({K * R * k / (ms * K / 1e3) / 1e6:.1f} M entries/s)")
+    return {"step_ms": ms, "entries_per_s": R * k / (ms / 1e3), "miss_copy_GBps": m.sum() * w.row_bytes / K / (ms / 1e3) / 1e9,
+            "steps": K, "warmup": W}
 
 
 def gather_leg(hm, torch, np, sw, out, w, n, hbm_copy):
@@ -510,6 +594,8 @@ def main() -> int:
     if args.split_steps != 0:
         rep["hit_path"] = split_leg(hm, torch, np, sw, topk, tail0, W, K if args.split_steps < 0 else args.split_steps,
                                     w, total_miss / K)
+    if args.split_steps != 0:
+        rep["overlap"] = overlap_leg(hm, torch, np, sw, topk, tail0, W, K if args.split_steps < 0 else args.split_steps, w)
     if args.trial_steps > 0:
         kt = min(args.trial_steps, K)
         rep["trial_commit"] = trial_leg(hm, torch, np, sw, topk, tail0, W, kt, w)
