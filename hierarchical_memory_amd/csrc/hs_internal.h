@@ -46,7 +46,7 @@ inline Layout make_layout(int k, int B, int H) {
   L.first = take(4ull * k);
   L.mpre = L.selpre;
   L.vict = L.first;
-  L.mtok = L.rank;
+  L.mtok = L.pos_slot;  // rank -> hit slot is dead once each position has taken its slot
   L.gsrc = take(4ull * k);
   L.misc = take(4ull * (4 * kWaves + 8));
   L.total = (uint32_t)off;

@@ -12,12 +12,14 @@
 //            classified (padding, bad, resident, candidate);
 //   phase 1  the selected set, and the candidates among it (not resident), as
 //            LDS bitmaps over token ids;
-//   phase 2  rank of every selected id among the selected ids (popcount prefix
-//            over the bitmap words); the lowest position of each rank is kept,
-//            so a repeated id is found without any order-dependent atomic;
-//   phase 3  every slot tests its token against the bitmap: a hit, found in O(1)
-//            through the token's rank, also marked in a hit bitmap, so the
-//            missed ids are the candidate bits without a hit bit;
+//   phase 2  popcount prefix over the selected bitmap's words, so the rank of a
+//            selected id among the selected ids is one lookup;
+//   phase 3  in one pass, every selected position takes its id's rank and bids
+//            for it (the lowest position wins, so a repeated id is found without
+//            any order-dependent atomic) while every slot tests its token
+//            against the bitmap: a hit, found in O(1) and recorded under the
+//            token's rank, also marked in a hit bitmap, so the missed ids are the
+//            candidate bits without a hit bit;
 //   phase 4  one block scan gives each missed id its rank among the misses
 //            (ascending id) and each non-hit slot its rank in the LRU order (the
 //            first m are the victims); the surviving candidates open the new
@@ -146,8 +148,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   const Layout& L = a.L;
   int32_t* ids = (int32_t*)(smem + L.ids);
   int8_t* cls = (int8_t*)(smem + L.cls);
-  int32_t* pos_slot = (int32_t*)(smem + L.pos_slot);  // position -> slot that holds its id (hit)
-  int32_t* rnk = (int32_t*)(smem + L.rank);           // position -> rank of its id among the selected ids
+  int32_t* rank_slot = (int32_t*)(smem + L.pos_slot);  // rank of a selected id -> slot that holds it (hit)
+  int32_t* rnk = (int32_t*)(smem + L.rank);  // position -> rank of its id, then -> its slot (hit) or -1
   int32_t* stok = (int32_t*)(smem + L.stok);
   uint16_t* ord = (uint16_t*)(smem + L.ord);
   uint8_t* sflag = smem + L.sflag;  // 1: hit this step, 2: victim this step
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   };
   auto ids4 = [&](int i, int4 x) {
     reinterpret_cast<int4*>(ids)[i] = x;
-    reinterpret_cast<int4*>(pos_slot)[i] = make_int4(-1, -1, -1, -1);
+    reinterpret_cast<int4*>(rank_slot)[i] = make_int4(-1, -1, -1, -1);
     const uint32_t c = (uint32_t)(uint8_t)classify(x.x) | ((uint32_t)(uint8_t)classify(x.y) << 8) |
                        ((uint32_t)(uint8_t)classify(x.z) << 16) | ((uint32_t)(uint8_t)classify(x.w) << 24);
     reinterpret_cast<uint32_t*>(cls)[i] = c;
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       const int32_t x = a.topk[rk + i];
       ids[i] = x;
       cls[i] = classify(x);
-      pos_slot[i] = -1;
+      rank_slot[i] = -1;
     }
   }
   bad = __syncthreads_or(bad);
@@ -275,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   }
   __syncthreads();
 
-  // ---- phase 2: rank of each selected id; the lowest position of each rank wins
+  // ---- phase 2: prefix counts of the selected bitmap (the rank of a selected id is one lookup)
   {
     int cnt = 0;
     for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
@@ -287,6 +289,10 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     }
   }
   __syncthreads();
+
+  // ---- phase 3: ranks and the hit test in one pass. Every selected position records the rank of its id and
+  // bids for it (the lowest position holding an id wins); every slot whose token is selected records itself
+  // under that token's rank and marks the token hit.
   for (int i = tid; i < k; i += kThreads) {
     const int8_t c = cls[i];
     if (c == C_CAND || c == C_RES) {
@@ -296,29 +302,33 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       atomicMin(&first[q], i);
     }
   }
-  __syncthreads();
-
-  // ---- phase 3: repeats, then the hit test: every slot looks its token up in the selected set
-  for (int i = tid; i < k; i += kThreads) {
-    const int8_t c = cls[i];
-    if ((c == C_CAND || c == C_RES) && first[rnk[i]] != i) {
-      cls[i] = C_DUP;
-      st |= kStatusDupId;
-    }
-  }
   for (int s = s0; s < s1; ++s) {
     const int32_t y = stok[s];
     if (y < 0 || resident(y)) continue;  // empty, or resident (a resident id takes no slot)
     const uint32_t word = sel[y >> 5];
     if (word & (1u << (y & 31))) {
-      const int q = (int)selpre[y >> 5] + __popc(word & below(y));
-      pos_slot[first[q]] = s;
+      rank_slot[(int)selpre[y >> 5] + __popc(word & below(y))] = s;
       sflag[s] = 1;
       atomicOr(&hbits[y >> 5], 1u << (y & 31));
     }
   }
-  if (st) atomicOr(&misc[kMiscStatus], st);
   __syncthreads();
+  // Repeats: a position that lost its rank's bid holds a repeated id. From here on a position's cls and rnk
+  // entries are read and written by its own thread only, so rnk takes the position's slot (hit) or -1, and
+  // phase 4 needs no barrier before it: it reads bitmaps, slot flags and the order list, final above.
+  for (int i = tid; i < k; i += kThreads) {
+    const int8_t c = cls[i];
+    if (c == C_CAND || c == C_RES) {
+      const int q = rnk[i];
+      if (first[q] != i) {
+        cls[i] = C_DUP;
+        st |= kStatusDupId;
+      } else {
+        rnk[i] = rank_slot[q];
+      }
+    }
+  }
+  if (st) atomicOr(&misc[kMiscStatus], st);
 
   // ---- phase 4: ranks of the misses (ascending id) and of the non-hit slots in LRU order, in one scan
   // (misses in the low 16 bits: m <= k <= 8192; candidates in the high 16 bits: <= B <= 65535)
@@ -375,7 +385,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     const int32_t x = ids[i];
     int32_t o = -1, g = -1;
     const bool cand = c == C_CAND;
-    if (cand && pos_slot[i] < 0) {  // a miss
+    const int32_t hit = cand ? rnk[i] : -1;
+    if (cand && hit < 0) {  // a miss
       const int w = x >> 5;
       const int j = (int)mpre[w] + __popc(cbits[w] & ~hbits[w] & below(x));
       const int v = vict[j];
@@ -395,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       o = v;
       g = -2 - j;
     } else if (cand) {  // a hit
-      o = pos_slot[i];
+      o = hit;
       g = o;
     } else if (c == C_RES) {
       o = B + x % T;  // the tail is a ring: token x in row x mod T
