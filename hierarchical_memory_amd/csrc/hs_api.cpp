@@ -106,6 +106,26 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 int check_ready(hs_ctx* ctx) {
   if (!ctx) return fail(HS_E_INVALID, "context is NULL");
   if (!ctx->bound) return fail(HS_E_STATE, "device buffers not bound (call hs_bind_device first)");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != ctx->device)
+    return fail(HS_E_STATE, "the context belongs to device %d but device %d is current", ctx->device, dev);
+  return HS_OK;
+}
+
+// A buffer handed to the kernels must be device (or managed) memory of the context's device.
+int check_device_buffer(const hs_ctx* ctx, const void* p, const char* name) {
+  hipPointerAttribute_t at{};
+  hipError_t e = hipPointerGetAttributes(&at, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(HS_E_INVALID, "buffer '%s' is not memory the HIP runtime knows (%s)", name, hipGetErrorString(e));
+  }
+  if (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeManaged)
+    return fail(HS_E_INVALID, "buffer '%s' is not device memory", name);
+  if (at.device != ctx->device)
+    return fail(HS_E_INVALID, "buffer '%s' lives on device %d, the context on device %d", name, at.device, ctx->device);
   return HS_OK;
 }
 
@@ -139,7 +159,10 @@ int hs_create(const hs_config* cfg, hs_ctx** out) {
   if ((int64_t)L.total + 1024 > (int64_t)lds_max)
     return fail(HS_E_INVALID, "this shape needs %u bytes of LDS per workgroup, the device allows %d", L.total,
                 lds_max);
-  e = hs::set_lds_limits(L.total, 4u * (uint32_t)cfg->device_buffer_size);
+  // The cap on dynamic LDS is an attribute of the kernels, shared by every context on the device: set it to
+  // the most any context may use, so a later context of a smaller shape cannot lower it under this one.
+  const uint32_t cap = std::min<uint32_t>(159u * 1024u, (uint32_t)lds_max - 1024u);
+  e = hs::set_lds_limits(cap, cap);
   if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(resolve kernel LDS)");
 
   hs_ctx* ctx = new (std::nothrow) hs_ctx();
@@ -199,6 +222,8 @@ int hs_bind_device(hs_ctx* ctx, const hs_device_views* v) {
                   (unsigned long long)n.need);
     if (!aligned(n.p, n.align)) return fail(HS_E_INVALID, "device buffer '%s' is not %d-byte aligned", n.name,
                                              (int)n.align);
+    const int rc = check_device_buffer(ctx, n.p, n.name);
+    if (rc) return rc;
   }
   if (ctx->cfg.tail_tokens > 0) {
     if (!v->tail) return fail(HS_E_INVALID, "device buffer 'tail' is NULL but tail_tokens = %d", ctx->cfg.tail_tokens);
@@ -206,6 +231,8 @@ int hs_bind_device(hs_ctx* ctx, const hs_device_views* v) {
       return fail(HS_E_INVALID, "device buffer 'tail' has %llu bytes, needs %llu", (unsigned long long)v->tail_bytes,
                   (unsigned long long)s.tail_bytes);
     if (!aligned(v->tail, 16)) return fail(HS_E_INVALID, "device buffer 'tail' is not 16-byte aligned");
+    const int rc = check_device_buffer(ctx, v->tail, "tail");
+    if (rc) return rc;
   }
   ctx->views = *v;
   ctx->bound = true;

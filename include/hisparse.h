@@ -51,7 +51,8 @@ extern "C" {
 #define HS_E_INVALID (-1) /* bad argument: null pointer, size out of range, buffer too small, B < k ... */
 #define HS_E_NOMEM (-2)   /* the pinned host pool could not be allocated */
 #define HS_E_HIP (-3)     /* a HIP runtime call failed (no device, launch failure, attribute) */
-#define HS_E_STATE (-4)   /* call out of order (e.g. resolve before hs_bind_device) */
+#define HS_E_STATE (-4)   /* call out of order (e.g. resolve before hs_bind_device), or made while another
+                             device than the context's is current */
 
 /* Per-request status bits written by hs_resolve. */
 #define HS_STATUS_BAD_ID 1    /* an id outside [0, host_rows), or >= tail0 but outside the tail window */
@@ -123,14 +124,19 @@ typedef struct hs_ctx hs_ctx;
 int hs_required_sizes(const hs_config* cfg, hs_sizes* out);
 
 /* Validate cfg, allocate the pinned mapped host pool on the current HIP device
- * (contents undefined until the caller fills it) and return a context. */
+ * (contents undefined until the caller fills it) and return a context. The context belongs to that device:
+ * every later call on it must be made while the same device is current (else HS_E_STATE). */
 int hs_create(const hs_config* cfg, hs_ctx** out);
 
 /* Host address of the pool: request r's row x starts at
  * host_base + r * request_stride_bytes + x * row_bytes. */
 int hs_host_pool(hs_ctx* ctx, void** host_base, uint64_t* request_stride_bytes, int32_t* host_rows);
 
-/* Register the caller's device buffers (checked against the sizes). Must precede reset/resolve/gather. */
+/* Register the caller's device buffers. Each must be device (or managed) memory of the context's device,
+ * at least the size hs_required_sizes gives and aligned to its element (16 bytes for hot and tail);
+ * HS_E_INVALID names the first that is not. Must precede reset/resolve/gather. The per-call device
+ * buffers (ids, outputs, plans, trial records, gather outputs) are not checked this way: they must be
+ * device memory of the same device too. */
 int hs_bind_device(hs_ctx* ctx, const hs_device_views* views);
 
 /* Reset requests to the empty state: slot table, stamps and page table -1, LRU order = slot order,

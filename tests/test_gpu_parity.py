@@ -236,6 +236,41 @@ def test_graph_replay_equals_eager():
     graph.close()
 
 
+def test_two_contexts_of_different_shapes():
+    """A context keeps working after another one of a smaller shape (less LDS) is created on the device."""
+    big = Pair(workload.GROW_32.with_(num_requests=4, steps=6))
+    small = Pair(workload.SINGLE_4K.with_(steps=6, top_k=16, buffer_slots=32, host_rows=64, L0=64, window=64))
+    for _ in range(6):
+        big.step()
+        small.step()
+    big.check_state()
+    small.check_state()
+    big.close()
+    small.close()
+
+
+def test_bind_rejects_host_memory():
+    """Binding checks that every buffer is device memory of the context's device."""
+    import hierarchical_memory_amd as hm
+    cfg = hm.config(2, 8, 16, 0.0, 64, 32)
+    ctx = hm.hs_create(cfg)
+    try:
+        dev = dict(hot=torch.zeros((2, 16, 64), dtype=torch.uint8, device="cuda"), tail=None,
+                   slot_tok=torch.empty((2, 16), dtype=torch.int32, device="cuda"),
+                   stamp=torch.empty((2, 16), dtype=torch.int32, device="cuda"),
+                   lru_order=torch.empty((2, 16), dtype=torch.int16, device="cuda"),
+                   page=torch.empty((2, 32), dtype=torch.int32, device="cuda"),
+                   step=torch.empty((2,), dtype=torch.int32, device="cuda"))
+        for host in (torch.empty((2, 32), dtype=torch.int32),
+                     torch.empty((2, 32), dtype=torch.int32, pin_memory=True)):
+            with pytest.raises(hm.HiSparseError) as err:
+                hm.hs_bind_device(ctx, **dict(dev, page=host))
+            assert err.value.code == hm.HS_E_INVALID and "page" in str(err.value)
+        hm.hs_bind_device(ctx, **dev)  # all device memory: accepted
+    finally:
+        hm.hs_destroy(ctx)
+
+
 def test_largest_shape_that_fits_lds():
     """Near the LDS limit of one workgroup: a wide buffer and a long context."""
     import hierarchical_memory_amd as hm
