@@ -333,6 +333,13 @@ MUTANTS = {
     "step counter not advanced": ("*t_io = t + 1;", "*t_io = t;"),
     "FIFO refreshes hit stamps": ("if (d->policy == ORACLE_LRU)\n    for", "if (1)\n    for"),
     "LRU leaves hit stamps alone": ("if (d->policy == ORACLE_LRU)\n    for", "if (d->policy == ORACLE_FIFO)\n    for"),
+    "offload leaves the hot slot stale": (
+        "if (page[x] != -1) memcpy(hot + (int64_t)page[x] * rb, rows + (int64_t)j * rb, (size_t)rb);", ""),
+    "offloaded rows in reverse order": ("memcpy(host + x * rb, rows + (int64_t)j * rb, (size_t)rb);",
+                                        "memcpy(host + x * rb, rows + (int64_t)(n - 1 - j) * rb, (size_t)rb);"),
+    "leaving tail rows not written to the host": ("memcpy(host + x * rb, tail + (x % d->T) * rb, (size_t)rb);", ""),
+    "tail window not advanced": ("*tail0 += n;", "*tail0 += 0;"),
+    "tail advance not clamped to the ring": ("if (n > d->T) n = d->T;", ""),
 }
 
 
@@ -363,6 +370,8 @@ def _run_pins_against(lib_path: str) -> bool:
                     for ids in seq:
                         _compare_with_list(o, lst, 0, list(ids)[::-1])
         me.test_cold_start()
+        me.test_offload_keeps_slots_consistent()
+        me.test_advance_tail_moves_rows_to_host()
         me.test_buffer_equals_topk()
         me.test_error_paths()
         me.test_fifo_closed_forms()
