@@ -58,6 +58,35 @@ def test_tiny_random(k, B, H, T, rb):
     p.close()
 
 
+def _random_shape(seed):
+    rng = np.random.default_rng(10_000 + seed)
+    k = int(rng.integers(1, 700))
+    B = int(rng.integers(k, 3 * k + 2))
+    H = int(rng.integers(max(B // 2, 2), 4 * B + 8))
+    T = int(rng.integers(1, 64)) if rng.random() < 0.4 else 0
+    rb = int(rng.choice([16, 48, 80, 1152, 16 * int(rng.integers(1, 160))]))
+    R = int(rng.integers(1, 24))
+    policy = int(rng.integers(0, 2))
+    gather = bool(rng.random() < 0.5)
+    return rng, R, k, B, H, T, rb, policy, gather
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes(seed):
+    """Seeded random shapes (k, B, context, tail, row size, policy, fused gather), with padding, bad and repeated
+    ids, k and B off the 16-byte vector path; every step and the final state against the oracle."""
+    rng, R, k, B, H, T, rb, policy, gather = _random_shape(seed)
+    steps = 6
+    log(f"[random shape {seed}] R={R} k={k} B={B} H={H} T={T} rb={rb} policy={policy} gather={gather}")
+    w = workload.SINGLE_4K.with_(name=f"random_{seed}", num_requests=R, top_k=k, buffer_slots=B, host_rows=H, L0=H,
+                                 tail_tokens=T, row_elems=rb // 2, steps=steps, fused_gather=gather)
+    ids = _random_ids(rng, R, steps, k, H, p_weird=0.05)
+    tail0 = rng.integers(0, H + 1, size=R).astype(np.int32) if T else None
+    p = Pair(w, ids=ids, tail0=tail0, gather=gather, policy=policy)
+    p.run(check_every=2)
+    p.close()
+
+
 def test_single_request_full():
     p = Pair(workload.SINGLE_4K, gather=True)
     p.run(check_every=1)
