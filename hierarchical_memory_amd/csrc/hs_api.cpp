@@ -69,6 +69,13 @@ int check_config(const hs_config* cfg, int32_t* H_out, hs::Layout* L_out) {
     H = (int64_t)want;
   }
   if (H < 1) return fail(HS_E_INVALID, "host rows per request must be >= 1");
+  // The pool (R * H * row_bytes) is the one size that can pass 64 bits: bound it well below that, so no size
+  // or offset derived from it wraps (the allocation itself fails long before).
+  uint64_t pool = 0;
+  if (__builtin_mul_overflow((uint64_t)cfg->num_requests, (uint64_t)H, &pool) ||
+      __builtin_mul_overflow(pool, (uint64_t)cfg->row_bytes, &pool) || pool > (1ull << 56))
+    return fail(HS_E_INVALID, "the host pool (%d requests x %lld rows x %d bytes) exceeds 2^56 bytes",
+                cfg->num_requests, (long long)H, cfg->row_bytes);
   const hs::Layout L = hs::make_layout(cfg->top_k, cfg->device_buffer_size, (int)H);
   // 1 KiB of the 160 KiB of a gfx950 compute unit stays for the kernel's static LDS
   if (L.total > 159u * 1024u)

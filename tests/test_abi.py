@@ -42,6 +42,9 @@ def test_every_declared_symbol_is_exported():
     (dict(max_context=-5), "max_context"),
     (dict(device_buffer_size=40000, max_context=1 << 20), "LDS"),
     (dict(eviction_policy=2), "eviction_policy"),
+    # R x H x row_bytes ~ 2^67 would wrap a 64-bit size
+    (dict(num_requests=65535, top_k=8, device_buffer_size=8, max_context=2**31 - 1, row_bytes=1 << 20), "host pool"),
+    (dict(num_requests=65535, top_k=8, device_buffer_size=8, max_context=1 << 24, row_bytes=1 << 20), "host pool"),
 ])
 def test_bad_config_rejected(kw, msg):
     base = dict(num_requests=4, top_k=256, device_buffer_size=512, host_to_device_ratio=8.0, row_bytes=1152,
