@@ -69,6 +69,8 @@ def parse():
                     help="timed launches of hs_gather on the last step's selection (0: skip)")
     ap.add_argument("--offload-launches", type=int, default=32,
                     help="timed launches of hs_offload (and hs_advance_tail on workloads with a device tail); 0: skip")
+    ap.add_argument("--graph-steps", type=int, default=256,
+                    help="steps captured in one HIP graph and replayed (0: skip)")
     ap.add_argument("--trial-steps", type=int, default=256,
                     help="steps of the hs_trial + hs_commit leg after a reset (0: skip)")
     ap.add_argument("--split-steps", type=int, default=-1,
@@ -293,6 +295,41 @@ def overlap_leg(hm, torch, np, sw, topk, tail0, W, K, w):
     log(f"[bench] overlapped split: {ms:.3f} ms/step ({K * R * k / (ms * K / 1e3) / 1e6:.1f} M entries/s)")
     return {"step_ms": ms, "entries_per_s": R * k / (ms / 1e3), "miss_copy_GBps": m.sum() * w.row_bytes / K / (ms / 1e3) / 1e9,
             "steps": K, "warmup": W}
+
+
+def graph_leg(hm, torch, np, sw, topk, tail0, W, K, w, eager_miss):
+    """The same stream from a reset, its K timed steps captured as one HIP graph (one hs_resolve node per step,
+    each on its own staged ids) and replayed once between two events: the per-launch host overhead is gone,
+    which is what decides small workloads. The miss counts must equal the eager run's."""
+    R, k = w.num_requests, w.top_k
+    sw.reset()
+    out = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    miss = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
+    status = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
+    g = torch.empty((R, k, w.row_bytes), dtype=torch.uint8, device="cuda") if w.fused_gather else None
+    stream = torch.cuda.current_stream()
+    for t in range(W):
+        hm.hs_resolve(sw.ctx, topk[t], tail0, out, miss[t], status[t], g, stream)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(K):
+            hm.hs_resolve(sw.ctx, topk[W + i], tail0, out, miss[W + i], status[W + i], g, side)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    if status[W:].cpu().numpy().any():
+        raise SystemExit("device status bits set during the graph leg")
+    same = bool((miss[W:W + K].cpu().numpy() == eager_miss[:K]).all())
+    ms = start.elapsed_time(end) / K
+    del graph
+    log(f"[bench] graph: {ms * 1e3:.1f} us/step ({R * k / (ms / 1e3) / 1e6:.1f} M entries/s) over {K} captured steps")
+    return {"step_ms": ms, "entries_per_s": R * k / (ms / 1e3), "steps": K, "warmup": W, "same_misses_as_eager": same}
 
 
 def gather_leg(hm, torch, np, sw, out, w, n, hbm_copy):
@@ -609,6 +646,9 @@ def main() -> int:
         "hbm": {"achieved": hbm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hbm_gbps / HBM_PEAK_GBPS,
                 "algorithmic_bytes_per_launch": hbm_bytes},
     }
+    if args.graph_steps > 0:
+        kg = min(args.graph_steps, K)
+        rep["graph"] = graph_leg(hm, torch, np, sw, topk, tail0, W, kg, w, m)
     if args.gather_launches > 0:
         rep["gather"] = gather_leg(hm, torch, np, sw, out, w, args.gather_launches, hbm_copy)
     if args.split_steps != 0:
