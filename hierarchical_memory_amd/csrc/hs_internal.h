@@ -19,7 +19,7 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte ch
 // phase 4 on, the per-position ranks hold the missed ids from phase 5 on, and the prefix counts of the
 // selected set become the prefix counts of the misses.
 struct Layout {
-  uint32_t ids, cls, pos_slot, rank, stok, ord, sflag, sel, cbits, hbits, selpre, first, mpre, vict, mtok, gsrc,
+  uint32_t ids, cls, rank_slot, rank, stok, ord, sflag, sel, cbits, hbits, selpre, first, mpre, vict, mtok, gsrc,
       misc;
   uint32_t words;  // bitmap words = ceil(H / 32)
   uint32_t total;
@@ -34,7 +34,7 @@ inline Layout make_layout(int k, int B, int H) {
   auto take = [&](uint64_t bytes) { uint32_t o = (uint32_t)off; off = align16(off + bytes); return o; };
   L.ids = take(4ull * k);
   L.cls = take(1ull * k);
-  L.pos_slot = take(4ull * k);
+  L.rank_slot = take(4ull * k);
   L.rank = take(4ull * k);
   L.stok = take(4ull * B);
   L.ord = take(2ull * B);
@@ -46,7 +46,7 @@ inline Layout make_layout(int k, int B, int H) {
   L.first = take(4ull * k);
   L.mpre = L.selpre;
   L.vict = L.first;
-  L.mtok = L.pos_slot;  // rank -> hit slot is dead once each position has taken its slot
+  L.mtok = L.rank_slot;  // rank -> hit slot is dead once each position has taken its slot
   L.gsrc = take(4ull * k);
   L.misc = take(4ull * (4 * kWaves + 8));
   L.total = (uint32_t)off;

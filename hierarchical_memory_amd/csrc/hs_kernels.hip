@@ -148,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   const Layout& L = a.L;
   int32_t* ids = (int32_t*)(smem + L.ids);
   int8_t* cls = (int8_t*)(smem + L.cls);
-  int32_t* rank_slot = (int32_t*)(smem + L.pos_slot);  // rank of a selected id -> slot that holds it (hit)
+  int32_t* rank_slot = (int32_t*)(smem + L.rank_slot);  // rank of a selected id -> slot that holds it (hit)
   int32_t* rnk = (int32_t*)(smem + L.rank);  // position -> rank of its id, then -> its slot (hit) or -1
   int32_t* stok = (int32_t*)(smem + L.stok);
   uint16_t* ord = (uint16_t*)(smem + L.ord);
