@@ -9,25 +9,26 @@
 // Mixed Residency:
 //   phase 0  coalesced loads of the selected ids, the slot->token table and the
 //            LRU order list into LDS, all issued before any is consumed; ids
-//            classified (padding, bad, resident, candidate);
-//   phase 1  the selected set, and the candidates among it (not resident), as
-//            LDS bitmaps over token ids;
-//   phase 2  popcount prefix over the selected bitmap's words, so the rank of a
+//            classified (padding, bad, resident, candidate) and put straight
+//            into LDS bitmaps over token ids: the selected set, and the
+//            candidates among it (not resident);
+//   phase 1  popcount prefix over the selected bitmap's words, so the rank of a
 //            selected id among the selected ids is one lookup;
-//   phase 3  in one pass, every selected position takes its id's rank and bids
-//            for it (the lowest position wins, so a repeated id is found without
-//            any order-dependent atomic) while every slot tests its token
+//   phase 2  in one pass, every selected position takes its id's rank and, when
+//            phase 0 saw an id twice, bids for it (the lowest position wins, so a
+//            repeated id is resolved without any order-dependent atomic) while
+//            every slot tests its token
 //            against the bitmap: a hit, found in O(1) and recorded under the
 //            token's rank, also marked in a hit bitmap, so the missed ids are the
 //            candidate bits without a hit bit;
-//   phase 4  one block scan gives each missed id its rank among the misses
+//   phase 3  one block scan gives each missed id its rank among the misses
 //            (ascending id) and each non-hit slot its rank in the LRU order (the
 //            first m are the victims); the surviving candidates open the new
 //            LRU order;
-//   phase 5  j-th missed id -> j-th victim: page table, slot table, stamps,
+//   phase 4  j-th missed id -> j-th victim: page table, slot table, stamps,
 //            outputs; the hit and victim slots close the new LRU order in slot
 //            order;
-//   phase 6  wavefronts copy the missed rows, 16 bytes per lane, straight from
+//   phase 5  wavefronts copy the missed rows, 16 bytes per lane, straight from
 //            mapped pinned host memory into the HBM slots (and every selected
 //            row into the gather output when fused).
 // Scans run over thread-contiguous chunks: a DPP scan inside each wave, one
@@ -57,7 +58,8 @@ constexpr int kStatusBadId = 1, kStatusDupId = 2, kStatusBadState = 4, kStatusSt
 constexpr int kUnroll = 4;  // 16-byte loads each thread keeps in flight in the gather loop
 
 // misc words in LDS: one slot array of wave totals per block scan, then the status word
-constexpr int kMiscScanSel = 0, kMiscScanRank = kWaves, kMiscScanTail = 2 * kWaves, kMiscStatus = 3 * kWaves;
+constexpr int kMiscScanSel = 0, kMiscScanRank = kWaves, kMiscScanTail = 2 * kWaves, kMiscStatus = 3 * kWaves,
+              kMiscRepeat = 3 * kWaves + 1;
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2, 4, 8 inside each row of 16
 // lanes, then the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).
@@ -183,10 +185,11 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   auto resident = [&](int32_t x) { return has_tail && x >= t0 && (int64_t)x - (int64_t)t0 < (int64_t)T; };
   int st = 0;
 
-  // ---- phase 0: stage and classify. The first round of every global load of the phase is issued
-  // before any of them is consumed (one HBM round trip for the common shapes), as 16-byte vectors when the
-  // sizes allow; LDS scratch is cleared while they are in flight.
-  int bad = 0;
+  // ---- phase 0: stage and classify, and build the selected and candidate bitmaps. The first round of every
+  // global load of the phase is issued before any of them is consumed (one HBM round trip for the common
+  // shapes), as 16-byte vectors when the sizes allow; LDS scratch is cleared, behind a barrier, while they are
+  // in flight, so each id goes into the bitmaps straight from the register it arrives in.
+  int bad = 0, repeat = 0;
   const bool vecB = (B & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.slot_tok + rB) & 15) == 0) &&
                     ((reinterpret_cast<uintptr_t>(a.order + rB) & 7) == 0);
   const bool veck = (k & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.topk + rk) & 15) == 0);
@@ -200,7 +203,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   if (tid < n4k) x0 = tk4[tid];
   for (int w = tid; w < W; w += kThreads) { sel[w] = 0u; cbits[w] = 0u; hbits[w] = 0u; }
   for (int i = tid; i < k; i += kThreads) first[i] = INT_MAX;
-  if (tid == 0) misc[kMiscStatus] = 0;
+  if (tid == 0) { misc[kMiscStatus] = 0; misc[kMiscRepeat] = 0; }
+  __syncthreads();
 
   auto stage4 = [&](int i, int4 y, uint2 o) {
     reinterpret_cast<int4*>(stok)[i] = y;
@@ -221,12 +225,25 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     }
     return C_CAND;
   };
+  // a selected id (candidate or resident) goes into the selected bitmap, a candidate also into the candidate
+  // bitmap; finding its bit already set means the selection repeats an id
+  auto mark = [&](int32_t x, int8_t c) {
+    if (c == C_CAND || c == C_RES) {
+      const uint32_t bit = 1u << (x & 31);
+      if (atomicOr(&sel[x >> 5], bit) & bit) repeat = 1;
+      if (c == C_CAND) atomicOr(&cbits[x >> 5], bit);
+    }
+  };
   auto ids4 = [&](int i, int4 x) {
     reinterpret_cast<int4*>(ids)[i] = x;
     reinterpret_cast<int4*>(rank_slot)[i] = make_int4(-1, -1, -1, -1);
-    const uint32_t c = (uint32_t)(uint8_t)classify(x.x) | ((uint32_t)(uint8_t)classify(x.y) << 8) |
-                       ((uint32_t)(uint8_t)classify(x.z) << 16) | ((uint32_t)(uint8_t)classify(x.w) << 24);
-    reinterpret_cast<uint32_t*>(cls)[i] = c;
+    const int8_t cx = classify(x.x), cy = classify(x.y), cz = classify(x.z), cw = classify(x.w);
+    reinterpret_cast<uint32_t*>(cls)[i] = (uint32_t)(uint8_t)cx | ((uint32_t)(uint8_t)cy << 8) |
+                                          ((uint32_t)(uint8_t)cz << 16) | ((uint32_t)(uint8_t)cw << 24);
+    mark(x.x, cx);
+    mark(x.y, cy);
+    mark(x.z, cz);
+    mark(x.w, cw);
   };
 
   if (tid < n4B) stage4(tid, y0, o0);
@@ -246,12 +263,16 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   if (!veck) {
     for (int i = tid; i < k; i += kThreads) {
       const int32_t x = a.topk[rk + i];
+      const int8_t c = classify(x);
       ids[i] = x;
-      cls[i] = classify(x);
+      cls[i] = c;
       rank_slot[i] = -1;
+      mark(x, c);
     }
   }
+  if (repeat) misc[kMiscRepeat] = 1;
   bad = __syncthreads_or(bad);
+  const bool repeats = misc[kMiscRepeat] != 0;  // rare: only then do positions bid for their id's rank
 
   if (bad) {
     // impossible state: leave the request untouched
@@ -266,18 +287,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     return;
   }
 
-  // ---- phase 1: the selected set (candidate and resident ids) and the candidates as bitmaps
-  for (int i = tid; i < k; i += kThreads) {
-    const int8_t c = cls[i];
-    if (c == C_CAND || c == C_RES) {
-      const int32_t x = ids[i];
-      atomicOr(&sel[x >> 5], 1u << (x & 31));
-      if (c == C_CAND) atomicOr(&cbits[x >> 5], 1u << (x & 31));
-    }
-  }
-  __syncthreads();
-
-  // ---- phase 2: prefix counts of the selected bitmap (the rank of a selected id is one lookup)
+  // ---- phase 1: prefix counts of the selected bitmap (the rank of a selected id is one lookup)
   {
     int cnt = 0;
     for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
@@ -290,16 +300,16 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   }
   __syncthreads();
 
-  // ---- phase 3: ranks and the hit test in one pass. Every selected position records the rank of its id and
-  // bids for it (the lowest position holding an id wins); every slot whose token is selected records itself
-  // under that token's rank and marks the token hit.
+  // ---- phase 2: ranks and the hit test in one pass. Every selected position records the rank of its id and,
+  // if the selection repeats an id, bids for it (the lowest position holding an id wins); every slot whose
+  // token is selected records itself under that token's rank and marks the token hit.
   for (int i = tid; i < k; i += kThreads) {
     const int8_t c = cls[i];
     if (c == C_CAND || c == C_RES) {
       const int32_t x = ids[i];
       const int q = (int)selpre[x >> 5] + __popc(sel[x >> 5] & below(x));
       rnk[i] = q;
-      atomicMin(&first[q], i);
+      if (repeats) atomicMin(&first[q], i);
     }
   }
   for (int s = s0; s < s1; ++s) {
@@ -315,12 +325,12 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   __syncthreads();
   // Repeats: a position that lost its rank's bid holds a repeated id. From here on a position's cls and rnk
   // entries are read and written by its own thread only, so rnk takes the position's slot (hit) or -1, and
-  // phase 4 needs no barrier before it: it reads bitmaps, slot flags and the order list, final above.
+  // phase 3 needs no barrier before it: it reads bitmaps, slot flags and the order list, final above.
   for (int i = tid; i < k; i += kThreads) {
     const int8_t c = cls[i];
     if (c == C_CAND || c == C_RES) {
       const int q = rnk[i];
-      if (first[q] != i) {
+      if (repeats && first[q] != i) {
         cls[i] = C_DUP;
         st |= kStatusDupId;
       } else {
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   }
   if (st) atomicOr(&misc[kMiscStatus], st);
 
-  // ---- phase 4: ranks of the misses (ascending id) and of the non-hit slots in LRU order, in one scan
+  // ---- phase 3: ranks of the misses (ascending id) and of the non-hit slots in LRU order, in one scan
   // (misses in the low 16 bits: m <= k <= 8192; candidates in the high 16 bits: <= B <= 65535)
   int m, ncand;
   {
@@ -378,7 +388,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   }
   __syncthreads();
 
-  // ---- phase 5: pair misses with victims: outputs and page table; the victims' new tokens go to the LDS
+  // ---- phase 4: pair misses with victims: outputs and page table; the victims' new tokens go to the LDS
   // copy of the slot table, written back below as coalesced rows
   for (int i = tid; i < k; i += kThreads) {
     const int8_t c = cls[i];
@@ -454,7 +464,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
 
   if (kMode == kTrial && tid == 0) trial_header(a, r, m, tail_start, t);
 
-  // ---- phase 6: rows (the block scan above ended with a barrier, so mtok and gsrc are visible)
+  // ---- phase 5: rows (the block scan above ended with a barrier, so mtok and gsrc are visible)
   const int row16 = a.row16;
   const v4u* hostr = a.host + rH * (size_t)row16;
   v4u* hotr = a.hot + rB * (size_t)row16;
