@@ -220,7 +220,7 @@ def _oracle_all_cores(w, sub, host, tail, tail0, policy, n_steps):
             "sample": f"the same {n_req} requests x {n_steps} steps on {cores} threads ({dt:.1f} s)", "cpu_model": model}
 
 
-def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step):
+def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step, hbm_copy=None):
     """The same stream again from a reset, as hs_plan + hs_copy on one stream. The plan kernel carries all the
     metadata work of a step (hit test, ranks, victims, page/slot tables, stamps, outputs) and no rows, so its
     duration prices the hit path against HBM."""
@@ -277,6 +277,7 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step):
         f"whole step {total_ms / K:.3f} ms")
     return {"kernel": "resolve_kernel<plan> (hs_plan)", "bound": "hbm", "achieved": hit_gbps, "peak": HBM_PEAK_GBPS,
             "unit": "GB/s", "frac": hit_gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": meta,
+            "frac_of_measured_hbm_copy": (hit_gbps / hbm_copy) if hbm_copy else None,
             "avg_launch_us": plan_avg * 1e3, "timing": "K plans back to back between two events",
             "avg_launch_us_between_copies": event_avg * 1e3, "p50_launch_us_between_copies": float(np.median(plan_ms)) * 1e3,
             "chain_same_misses": same_chain,
@@ -697,7 +698,7 @@ def main() -> int:
         rep["gather"] = gather_leg(hm, torch, np, sw, out, w, args.gather_launches, hbm_copy)
     if args.split_steps != 0:
         rep["hit_path"] = split_leg(hm, torch, np, sw, topk, tail0, W, K if args.split_steps < 0 else args.split_steps,
-                                    w, total_miss / K)
+                                    w, total_miss / K, hbm_copy)
     if args.split_steps != 0:
         rep["overlap"] = overlap_leg(hm, torch, np, sw, topk, tail0, W, K if args.split_steps < 0 else args.split_steps, w)
     if args.trial_steps > 0:
