@@ -116,10 +116,10 @@ def copy_probes(hm, torch, np, sw, w, reps: int = 7):
     R, k, B, H, rb = w.num_requests, w.top_k, w.buffer_slots, w.host_rows, w.row_bytes
     m = min(k, H)
     rng = np.random.default_rng(7)
-    seq = np.zeros((R, 2, k), np.int32)
+    seq = np.full((R, 3, k), -1, np.int32)  # the plan layout of hs_plan: tokens, slots, row sources
     seq[:, 0, :m] = np.arange(m, dtype=np.int32)
     seq[:, 1, :m] = np.arange(m, dtype=np.int32)
-    rnd = np.zeros((R, 2, k), np.int32)
+    rnd = np.full((R, 3, k), -1, np.int32)
     for r in range(R):
         rnd[r, 0, :m] = rng.choice(H, size=m, replace=False)
         rnd[r, 1, :m] = rng.choice(B, size=m, replace=False)
@@ -233,7 +233,7 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step, hbm_c
     status = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
     for t in range(W):
         hm.hs_plan(sw.ctx, topk[t], tail0, out, miss[t], status[t], plan, stream)
-        hm.hs_copy(sw.ctx, plan, miss[t], stream)
+        hm.hs_copy(sw.ctx, plan, miss[t], stream=stream)
     torch.cuda.synchronize()
     ea = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     eb = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
@@ -241,7 +241,7 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step, hbm_c
         ea[i].record(stream)
         hm.hs_plan(sw.ctx, topk[W + i], tail0, out, miss[W + i], status[W + i], plan, stream)
         eb[i].record(stream)
-        hm.hs_copy(sw.ctx, plan, miss[W + i], stream)
+        hm.hs_copy(sw.ctx, plan, miss[W + i], stream=stream)
     ea[K].record(stream)
     torch.cuda.synchronize()
     plan_ms = np.array([ea[i].elapsed_time(eb[i]) for i in range(K)])
@@ -289,7 +289,8 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step, hbm_c
 def overlap_leg(hm, torch, np, sw, topk, tail0, W, K, w):
     """The split path pipelined over two streams from a reset: the plan of step t+1 runs on the launch stream
     while the copy of step t is still in flight on a second stream (plans double-buffered; a plan depends only
-    on the previous plan, whose metadata is final when it ends; copies stay in order on their stream)."""
+    on the previous plan, whose metadata is final when it ends; copies stay in order on their stream). On a
+    fused-gather workload the copy also gathers every selected row."""
     R, k = w.num_requests, w.top_k
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
@@ -298,6 +299,9 @@ def overlap_leg(hm, torch, np, sw, topk, tail0, W, K, w):
     outs = [torch.empty((R, k), dtype=torch.int32, device="cuda") for _ in range(2)]
     miss = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
     status = torch.zeros((W + K, R), dtype=torch.int32, device="cuda")
+    # a fused-gather workload gathers every selected row in the copy (one output: in a decode loop the step's
+    # consumer would read it before the next copy)
+    g = torch.empty((R, k, w.row_bytes), dtype=torch.uint8, device="cuda") if w.fused_gather else None
     copied = [None, None]
 
     def step(t):
@@ -308,7 +312,7 @@ def overlap_leg(hm, torch, np, sw, topk, tail0, W, K, w):
         planned = torch.cuda.Event()
         planned.record(main)
         side.wait_event(planned)
-        hm.hs_copy(sw.ctx, plans[b], miss[t], side)
+        hm.hs_copy(sw.ctx, plans[b], miss[t], g, stream=side)
         copied[b] = torch.cuda.Event()
         copied[b].record(side)
 
@@ -328,7 +332,7 @@ def overlap_leg(hm, torch, np, sw, topk, tail0, W, K, w):
     m = miss[W:].cpu().numpy().astype(np.int64)
     log(f"[bench] overlapped split: {ms:.3f} ms/step ({K * R * k / (ms * K / 1e3) / 1e6:.1f} M entries/s)")
     return {"step_ms": ms, "entries_per_s": R * k / (ms / 1e3), "miss_copy_GBps": m.sum() * w.row_bytes / K / (ms / 1e3) / 1e9,
-            "steps": K, "warmup": W}
+            "steps": K, "warmup": W, "gather": w.fused_gather}
 
 
 def graph_leg(hm, torch, np, sw, topk, tail0, W, K, w, eager_miss):

@@ -103,7 +103,7 @@ void fill_sizes(const hs_config* cfg, int32_t H, const hs::Layout& L, hs_sizes* 
   s->topk_bytes = R * k * 4;
   s->out_bytes = R * k * 4;
   s->gather_bytes = R * k * rb;
-  s->plan_bytes = R * 2 * k * 4;
+  s->plan_bytes = R * 3 * k * 4;
   s->trial_bytes = R * (uint64_t)hs::trial_words((int)k, (int)B) * 4;
   s->lds_bytes = L.total;
 }
@@ -375,20 +375,25 @@ int hs_commit(hs_ctx* ctx, const int32_t* d_trial, const void* d_gather, const i
   return ok();
 }
 
-int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* stream) {
+int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* d_gather, void* stream) {
   int rc = check_ready(ctx);
   if (rc) return rc;
   if (!d_plan || !d_miss) return fail(HS_E_INVALID, "plan and miss must not be NULL");
+  if (d_gather && !aligned(d_gather, 16)) return fail(HS_E_INVALID, "gather output is not 16-byte aligned");
   hs::CopyArgs a{};
   a.R = ctx->cfg.num_requests;
   a.k = ctx->cfg.top_k;
   a.B = ctx->cfg.device_buffer_size;
   a.H = ctx->H;
+  a.T = ctx->cfg.tail_tokens;
   a.row16 = ctx->cfg.row_bytes / 16;
+  a.rows = std::max(1, hs::kGatherChunks / a.row16);
   a.plan = d_plan;
   a.miss = d_miss;
   a.host = (const hs::v4u*)ctx->pool_dev;
   a.hot = (hs::v4u*)ctx->views.hot;
+  a.tail = (const hs::v4u*)ctx->views.tail;
+  a.gather = (hs::v4u*)d_gather;
   hipError_t e = hs::launch_copy(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "copy launch");
   return ok();

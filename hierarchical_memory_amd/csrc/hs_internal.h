@@ -72,7 +72,8 @@ struct ResolveArgs {
   int32_t* miss;
   int32_t* status;
   v4u* gather;
-  int32_t* plan;    // non-null: plan-only launch, [R][2][k] (missed tokens, then their victim slots)
+  int32_t* plan;    // non-null: plan-only launch, [R][3][k] (missed tokens, their victim slots, the source of
+                    // each position's row: slot, B + tail row, -1 none, -2 - j the j-th miss)
   int32_t* trial;   // non-null: trial launch, [R][trial_words]
   int64_t trial_words;
 };
@@ -97,11 +98,14 @@ struct CommitArgs {
 };
 
 struct CopyArgs {
-  int32_t R, k, B, H, row16;
-  const int32_t* plan;  // [R][2][k]
+  int32_t R, k, B, H, T, row16;
+  int32_t rows;         // with a gather: selected rows per workgroup
+  const int32_t* plan;  // [R][3][k]
   const int32_t* miss;  // [R]
   const v4u* host;
   v4u* hot;
+  const v4u* tail;      // [R][T][row16] or nullptr
+  v4u* gather;          // [R][k][row16] or nullptr (no gather)
 };
 
 struct OffloadArgs {

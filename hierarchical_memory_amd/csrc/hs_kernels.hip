@@ -424,6 +424,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     }
     a.out[rk + i] = o;
     gsrc[i] = g;
+    if (kMode == kPlan) a.plan[rk * 3 + 2 * k + i] = g;  // where position i's row comes from (hs_copy's gather)
   }
   // the slots used this step close the new order in slot order: hits and victims (LRU) or victims only
   // (FIFO); the scan's barrier also publishes the LDS writes above
@@ -451,8 +452,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
 
   if (kMode == kPlan) {
     for (int j = tid; j < m; j += kThreads) {
-      a.plan[rk * 2 + j] = mtok[j];
-      a.plan[rk * 2 + k + j] = vict[j];
+      a.plan[rk * 3 + j] = mtok[j];
+      a.plan[rk * 3 + k + j] = vict[j];
     }
     if (tid == 0) {
       a.step[r] = t + 1;
@@ -507,7 +508,10 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       for (int u = 0; u < kUnroll; ++u) {
         const int c = c0 + u * kThreads;
         if (c < total) {
-          gr[c] = v[u];
+          // streamed in a fused step (nothing reads the output back in this launch, and it leaves less to
+          // write back when the launch ends); plain in a trial, whose commit reads the missed rows back
+          if (kMode == kTrial) gr[c] = v[u];
+          else __builtin_nontemporal_store(v[u], gr + c);
           if (hot_dst[u] >= 0) hotr[hot_dst[u]] = v[u];
         }
       }
@@ -581,7 +585,7 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
   const int row16 = a.row16;
   const int total = m * row16;
   const size_t rk = (size_t)r * a.k;
-  const int32_t* ptok = a.plan + rk * 2;
+  const int32_t* ptok = a.plan + rk * 3;
   const int32_t* pslot = ptok + a.k;
   const v4u* hostr = a.host + (size_t)r * a.H * row16;
   v4u* hotr = a.hot + (size_t)r * a.B * row16;
@@ -591,6 +595,60 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
     const int x = ptok[j], s = pslot[j];
     if (x >= 0 && x < a.H && s >= 0 && s < a.B)
       hotr[(size_t)s * row16 + q] = load_host(hostr + (size_t)x * row16 + q);
+  }
+}
+
+// A plan's rows and the gather of every selected row, in the gather kernel's tiles: workgroup (b, r) fills
+// positions [b*rows, b*rows + rows) of request r's gather output, each 16-byte chunk from where the plan says
+// the position's row is: a missed row from the host pool (also written to its victim slot), a hot slot, a tail
+// row, or zeros. The host loads spread over every workgroup of the chip rather than one per request.
+__global__ __launch_bounds__(kGatherThreads) void copy_gather_kernel(CopyArgs a) {
+  const int r = blockIdx.y;
+  const int i0 = blockIdx.x * a.rows;
+  const int row16 = a.row16, k = a.k, B = a.B;
+  const int n = min(a.rows, k - i0) * row16;
+  const int m = a.miss[r];
+  const size_t rk = (size_t)r * k;
+  const int32_t* ptok = a.plan + rk * 3;
+  const int32_t* pslot = ptok + k;
+  const int32_t* psrc = ptok + 2 * k + i0;
+  const v4u* hostr = a.host + (size_t)r * a.H * row16;
+  v4u* hotr = a.hot + (size_t)r * B * row16;
+  const v4u* tailr = a.tail ? a.tail + (size_t)r * a.T * row16 : nullptr;
+  v4u* gr = a.gather + (rk + i0) * row16;
+  for (int c0 = threadIdx.x; c0 < n; c0 += kGatherThreads * kGatherUnroll) {
+    v4u v[kGatherUnroll];
+    int64_t slot_dst[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int c = c0 + u * kGatherThreads;
+      v[u] = v4u{0u, 0u, 0u, 0u};
+      slot_dst[u] = -1;
+      if (c >= n) continue;
+      const int i = (int)((unsigned)c / (unsigned)row16), q = c - i * row16;
+      const int g = psrc[i];
+      if (g <= -2) {
+        const int j = -2 - g;
+        if (j < m && m <= k) {
+          const int x = ptok[j], s = pslot[j];
+          if (x >= 0 && x < a.H && s >= 0 && s < B) {
+            v[u] = load_host(hostr + (size_t)x * row16 + q);
+            slot_dst[u] = (int64_t)s * row16 + q;
+          }
+        }
+      } else if (g >= B) {
+        if (g - B < a.T) v[u] = __builtin_nontemporal_load(tailr + (size_t)(g - B) * row16 + q);
+      } else if (g >= 0) {
+        v[u] = __builtin_nontemporal_load(hotr + (size_t)g * row16 + q);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int c = c0 + u * kGatherThreads;
+      if (c >= n) continue;
+      __builtin_nontemporal_store(v[u], gr + c);
+      if (slot_dst[u] >= 0) hotr[slot_dst[u]] = v[u];
+    }
   }
 }
 
@@ -789,6 +847,13 @@ hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
+  if (a.gather) {
+    if ((size_t)a.R * a.k * a.row16 == 0) return hipSuccess;
+    if (a.rows < 1) return hipErrorInvalidValue;
+    const unsigned bx = (unsigned)((a.k + a.rows - 1) / a.rows);
+    hipLaunchKernelGGL(copy_gather_kernel, dim3(bx, (unsigned)a.R), dim3(kGatherThreads), 0, s, a);
+    return hipGetLastError();
+  }
   // about 128K threads (one 16-byte host load in flight each) over the whole chip
   int g = (512 + a.R - 1) / a.R;
   if (g < 1) g = 1;

@@ -73,7 +73,7 @@ def lib():
         L.hs_reset.argtypes = [vp, vp, i32, vp]
         L.hs_resolve.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         L.hs_plan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
-        L.hs_copy.argtypes = [vp, vp, vp, vp]
+        L.hs_copy.argtypes = [vp, vp, vp, vp, vp]
         L.hs_trial.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.hs_commit.argtypes = [vp, vp, vp, vp, vp, vp]
         L.hs_offload.argtypes = [vp, vp, vp, i32, vp, vp]
@@ -179,8 +179,8 @@ def hs_plan(ctx, topk, tail0, out, miss, status, plan, stream=None) -> None:
                          _stream(stream)))
 
 
-def hs_copy(ctx, plan, miss, stream=None) -> None:
-    _check(lib().hs_copy(ctx, _ptr(plan), _ptr(miss), _stream(stream)))
+def hs_copy(ctx, plan, miss, gather=None, stream=None) -> None:
+    _check(lib().hs_copy(ctx, _ptr(plan), _ptr(miss), _ptr(gather), _stream(stream)))
 
 
 def hs_trial(ctx, topk, tail0, out, miss, status, gather, trial, stream=None) -> None:
@@ -271,7 +271,7 @@ class SwapIn:
 
     def plan_buffer(self):
         import torch
-        return torch.empty((self.R, 2, self.k), dtype=torch.int32, device=self.device)
+        return torch.empty((self.R, 3, self.k), dtype=torch.int32, device=self.device)
 
     def close(self) -> None:
         if self.ctx:

@@ -117,7 +117,7 @@ typedef struct hs_sizes {
   uint64_t topk_bytes;       /* [R][k] int32 input of one step */
   uint64_t out_bytes;        /* [R][k] int32 output of one step */
   uint64_t gather_bytes;     /* [R][k][row_bytes] gather output */
-  uint64_t plan_bytes;       /* [R][2][k] int32 miss list of hs_plan */
+  uint64_t plan_bytes;       /* [R][3][k] int32 plan of hs_plan (miss list and row sources) */
   uint64_t trial_bytes;      /* trial records of hs_trial / hs_commit */
   uint32_t lds_bytes;        /* LDS one resolve workgroup uses */
 } hs_sizes;
@@ -171,15 +171,19 @@ int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32
  * Memory", section 4 future work; 「HiSparse：階層化メモリシステムによるスパースアテンションの加速」, section
  * 「今後の展望」).
  * hs_plan does everything hs_resolve does except moving rows: outputs, page table, slot table, stamps and
- * step counters are final when it completes; d_plan [R][2][k] int32 receives, for request r, the missed
- * tokens in ascending id order (d_plan[r][0][0..m)) and their slots (d_plan[r][1][0..m)).
- * hs_copy then copies those rows from the host pool into the hot buffer. Until it completes, the hot rows
- * of this step's new slots are stale. Two plans may run back to back, but the copy of a step must complete
- * before the copy of the next step and before anything reads the hot rows.
+ * step counters are final when it completes; d_plan [R][3][k] int32 receives, for request r, the missed
+ * tokens in ascending id order (d_plan[r][0][0..m)), their slots (d_plan[r][1][0..m)) and, for every
+ * position i of the selection, where its row is (d_plan[r][2][i]: a slot in [0, B), B + a tail row, -1 for
+ * none, or -2 - j for the j-th miss).
+ * hs_copy then copies those rows from the host pool into the hot buffer. With d_gather (nullable,
+ * [R][k][row_bytes], 16-byte aligned) it also writes every selected row there, as hs_resolve's fused gather
+ * does, in workgroups spread over the whole chip (the missed rows straight from the host pool). Until it
+ * completes, the hot rows of this step's new slots are stale. Two plans may run back to back, but the copy
+ * of a step must complete before the copy of the next step and before anything reads the hot rows.
  */
 int hs_plan(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
             int32_t* d_status, int32_t* d_plan, void* stream);
-int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* stream);
+int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* d_gather, void* stream);
 
 /*
  * A retryable step, for speculative decoding: the vLLM page names a per-step resolver plan that can be

@@ -345,6 +345,35 @@ def test_plan_then_copy_matches_oracle():
     p.close()
 
 
+@pytest.mark.parametrize("tail", [False, True])
+def test_plan_then_copy_with_gather(tail):
+    """hs_plan, then hs_copy with a gather output: the gathered rows, the hot rows and every table equal the
+    oracle's fused step (padding, bad and repeated ids included; with and without a device tail)."""
+    import hierarchical_memory_amd as hm
+    rng = np.random.default_rng(31 + tail)
+    R, k, B, H, T, rb = 6, 200, 330, 1500, (40 if tail else 0), 80
+    steps = 8
+    w = workload.SINGLE_4K.with_(name=f"copy_gather_{tail}", num_requests=R, top_k=k, buffer_slots=B, host_rows=H,
+                                 L0=H, tail_tokens=T, row_elems=rb // 2, steps=steps, fused_gather=True)
+    ids = _random_ids(rng, R, steps, k, H, p_weird=0.05)
+    tail0 = rng.integers(H // 2, H - T, size=R).astype(np.int32) if T else None
+    p = Pair(w, ids=ids, tail0=tail0, gather=True)
+    out, miss, status, g = p.outs
+    plan = p.sw.plan_buffer()
+    for t in range(steps):
+        topk = torch.from_numpy(np.ascontiguousarray(ids[:, t])).cuda()
+        g.fill_(0xCD)
+        hm.hs_plan(p.sw.ctx, topk, p.tail0_dev, out, miss, status, plan)
+        hm.hs_copy(p.sw.ctx, plan, miss, g)
+        o_out, o_miss, o_st, o_g = p.o.step(ids[:, t], p.tail0, gather=True)
+        assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+        assert (status.cpu().numpy() == o_st).all()
+        assert (g.cpu().numpy() == o_g).all(), f"step {t}: gathered rows differ"
+        p.t += 1
+        p.check_state()
+    p.close()
+
+
 def test_copy_overlapped_on_second_stream():
     """Plans on the main stream, copies on a second stream, two steps in flight with double-buffered plans;
     after the last copy every table and every hot row equals the oracle's."""
@@ -367,7 +396,7 @@ def test_copy_overlapped_on_second_stream():
         planned = torch.cuda.Event()
         planned.record(main)
         side.wait_event(planned)
-        hm.hs_copy(p.sw.ctx, plans[b], misses[b], side)
+        hm.hs_copy(p.sw.ctx, plans[b], misses[b], stream=side)
         copied[b] = torch.cuda.Event()
         copied[b].record(side)
         o_out, o_miss, _, _ = p.o.step(p.ids[:, t])

@@ -1,6 +1,7 @@
 """GPU parity over random sequences of calls: every entry point of the C ABI interleaved on one context.
 
-Each sequence mixes fused resolves (with and without the gather), plan + copy, accepted and rejected trials,
+Each sequence mixes fused resolves (with and without the gather), plan + copy (with and without the gather),
+accepted and rejected trials,
 offloads, tail advances, partial resets and unfused gathers, in a seeded random order, on a small shape with a
 device tail. After every call its outputs and the whole device state (tables, stamps, step counters, hot rows,
 tail rows, tail starts, the host pool) must equal the oracle's, bit for bit.
@@ -28,8 +29,8 @@ import oracle  # noqa: E402
 import workload  # noqa: E402
 from tests.parity import Pair, log  # noqa: E402
 
-OPS = ("resolve", "resolve_gather", "plan_copy", "trial_accept", "trial_reject", "offload", "advance_tail",
-       "reset_some", "gather")
+OPS = ("resolve", "resolve_gather", "plan_copy", "plan_copy_gather", "trial_accept", "trial_reject", "offload",
+       "advance_tail", "reset_some", "gather")
 
 
 def _ids(rng, R, k, H):
@@ -89,13 +90,13 @@ def test_random_call_sequences(seed):
             op = "resolve"
         ids = _ids(rng, R, k, H)
         topk = torch.from_numpy(ids).cuda()
-        if op in ("resolve", "resolve_gather", "plan_copy", "trial_accept", "trial_reject"):
-            gather = op in ("resolve_gather", "trial_accept", "trial_reject")
+        if op in ("resolve", "resolve_gather", "plan_copy", "plan_copy_gather", "trial_accept", "trial_reject"):
+            gather = op in ("resolve_gather", "plan_copy_gather", "trial_accept", "trial_reject")
             if op in ("resolve", "resolve_gather"):
                 hm.hs_resolve(ctx, topk, p.tail0_dev, out, miss, status, g if gather else None)
-            elif op == "plan_copy":
+            elif op in ("plan_copy", "plan_copy_gather"):
                 hm.hs_plan(ctx, topk, p.tail0_dev, out, miss, status, plan)
-                hm.hs_copy(ctx, plan, miss)
+                hm.hs_copy(ctx, plan, miss, g if gather else None)
             else:
                 hm.hs_trial(ctx, topk, p.tail0_dev, out, miss, status, g, trial)
                 accept = torch.full((R,), 1 if op == "trial_accept" else 0, dtype=torch.int32, device="cuda")
