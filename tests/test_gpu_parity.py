@@ -407,6 +407,47 @@ def test_copy_overlapped_on_second_stream():
     p.close()
 
 
+def test_copy_with_gather_overlapped_on_second_stream():
+    """The pipelined step: plans on the main stream, copy-and-gather on a second stream, two steps in flight
+    (plans and gather outputs double-buffered); every gathered row and, at the end, every table and hot row
+    equal the oracle's."""
+    import hierarchical_memory_amd as hm
+    w = workload.HYBRID_64.with_(num_requests=6, steps=24)
+    p = Pair(w, sample=list(range(6)), gather=True)
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    R, k, rb = w.num_requests, w.top_k, w.row_bytes
+    plans = [p.sw.plan_buffer() for _ in range(2)]
+    misses = [torch.empty((R,), dtype=torch.int32, device="cuda") for _ in range(2)]
+    gathers = [torch.empty((R, k, rb), dtype=torch.uint8, device="cuda") for _ in range(2)]
+    out, _, status, _ = p.outs
+    copied = [None, None]
+    expected = [None, None]
+    topk_all = torch.from_numpy(np.ascontiguousarray(p.ids.transpose(1, 0, 2))).cuda()
+    torch.cuda.synchronize()
+    for t in range(w.steps):
+        b = t % 2
+        if copied[b] is not None:
+            copied[b].synchronize()  # the copy of step t - 2 is done: check its rows, then reuse its buffers
+            assert (gathers[b].cpu().numpy() == expected[b]).all(), f"step {t - 2}: gathered rows differ"
+        hm.hs_plan(p.sw.ctx, topk_all[t], p.tail0_dev, out, misses[b], status, plans[b], main)
+        planned = torch.cuda.Event()
+        planned.record(main)
+        side.wait_event(planned)
+        hm.hs_copy(p.sw.ctx, plans[b], misses[b], gathers[b], stream=side)
+        copied[b] = torch.cuda.Event()
+        copied[b].record(side)
+        o_out, o_miss, _, o_g = p.o.step(p.ids[:, t], p.tail0, gather=True)
+        expected[b] = o_g
+        assert (out.cpu().numpy() == o_out).all() and (misses[b].cpu().numpy() == o_miss).all()
+        p.t += 1
+    torch.cuda.synchronize()
+    for b in range(2):
+        assert (gathers[b].cpu().numpy() == expected[b]).all()
+    p.check_state()
+    p.close()
+
+
 def test_snapshot_restore_resume():
     """A snapshot of the seven device buffers, restored, resumes exactly like the uninterrupted run."""
     w = workload.GROW_32.with_(num_requests=4, steps=24)
