@@ -139,7 +139,15 @@ def hs_host_pool(ctx) -> Tuple[int, int, int]:
 
 
 def _ptr(t) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor argument. Every tensor the calls take is device memory read or written by a
+    kernel, so a tensor on the CPU (or with gaps) is refused here rather than handed to the GPU."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"expected a GPU tensor, got one on {t.device}")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
 
 
 def _bytes(t) -> int:
@@ -152,7 +160,7 @@ def hs_bind_device(ctx, hot, tail, slot_tok, stamp, lru_order, page, step) -> No
                     ("lru_order", lru_order), ("page", page), ("step", step)):
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-        setattr(v, name, _ptr(t))
+        setattr(v, name, None if t is None else t.data_ptr())  # the library checks these itself
         setattr(v, name + "_bytes", _bytes(t))
     _check(lib().hs_bind_device(ctx, ctypes.byref(v)))
 

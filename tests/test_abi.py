@@ -92,3 +92,13 @@ def test_sizes_of_the_workloads():
         assert s.host_pool_bytes == w.num_requests * w.host_rows * w.row_bytes
         assert s.lds_bytes <= 159 * 1024
         assert s.hot_bytes == w.num_requests * w.buffer_slots * w.row_bytes
+
+
+def test_binding_refuses_host_tensors():
+    """Per-call buffers must be GPU tensors: a CPU tensor is refused before anything reaches the library."""
+    import torch
+    cpu = torch.zeros(8, dtype=torch.int32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        hm.hs_resolve(None, cpu, None, cpu, cpu, cpu)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        hm.hs_gather(None, cpu, cpu)
