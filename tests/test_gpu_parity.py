@@ -345,19 +345,28 @@ def test_plan_then_copy_matches_oracle():
     p.close()
 
 
-@pytest.mark.parametrize("tail", [False, True])
-def test_plan_then_copy_with_gather(tail):
+COPY_GATHER_CASES = [  # (k, B, H, T, row_bytes, policy)
+    (200, 330, 1500, 0, 80, 0),
+    (200, 330, 1500, 40, 80, 0),  # device tail
+    (33, 40, 300, 7, 1152, 1),  # 10 rows per workgroup, the last of 4 holds 3; FIFO
+    (5, 8, 60, 3, 16384, 0),  # 1024 chunks per row: one row per workgroup in two passes
+]
+
+
+@pytest.mark.parametrize("k,B,H,T,rb,policy", COPY_GATHER_CASES,
+                         ids=[f"k{c[0]}_T{c[3]}_rb{c[4]}_p{c[5]}" for c in COPY_GATHER_CASES])
+def test_plan_then_copy_with_gather(k, B, H, T, rb, policy):
     """hs_plan, then hs_copy with a gather output: the gathered rows, the hot rows and every table equal the
-    oracle's fused step (padding, bad and repeated ids included; with and without a device tail)."""
+    oracle's fused step (padding, bad and repeated ids included; with and without a device tail; ragged and
+    large rows; both policies)."""
     import hierarchical_memory_amd as hm
-    rng = np.random.default_rng(31 + tail)
-    R, k, B, H, T, rb = 6, 200, 330, 1500, (40 if tail else 0), 80
-    steps = 8
-    w = workload.SINGLE_4K.with_(name=f"copy_gather_{tail}", num_requests=R, top_k=k, buffer_slots=B, host_rows=H,
-                                 L0=H, tail_tokens=T, row_elems=rb // 2, steps=steps, fused_gather=True)
+    rng = np.random.default_rng(31 + k + T)
+    R, steps = 6, 8
+    w = workload.SINGLE_4K.with_(name=f"copy_gather_k{k}_T{T}", num_requests=R, top_k=k, buffer_slots=B,
+                                 host_rows=H, L0=H, tail_tokens=T, row_elems=rb // 2, steps=steps, fused_gather=True)
     ids = _random_ids(rng, R, steps, k, H, p_weird=0.05)
     tail0 = rng.integers(H // 2, H - T, size=R).astype(np.int32) if T else None
-    p = Pair(w, ids=ids, tail0=tail0, gather=True)
+    p = Pair(w, ids=ids, tail0=tail0, gather=True, policy=policy)
     out, miss, status, g = p.outs
     plan = p.sw.plan_buffer()
     for t in range(steps):
