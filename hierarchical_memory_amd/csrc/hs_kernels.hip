@@ -659,6 +659,9 @@ __global__ __launch_bounds__(kGatherThreads) void copy_gather_kernel(CopyArgs a)
 __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint8_t* used = smem;  // B flags: slot in the new order's tail
+  // the misses' victim slots and gather positions, staged for the row copy (after the B flags, 4-aligned)
+  int32_t* lslot = reinterpret_cast<int32_t*>(smem + ((a.B + 3) & ~3));
+  int32_t* lpos = lslot + a.k;
   const int r = blockIdx.x, tid = threadIdx.x;
   if (a.accept && a.accept[r] == 0) {
     if (a.status && tid == 0) a.status[r] = 0;
@@ -689,18 +692,38 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   const int32_t* evicted = slot + k;
   const int32_t* pos = evicted + k;
   for (int j = tid; j < m; j += blockDim.x) {
-    const int x = tok[j], v = slot[j], y = evicted[j];
-    if (x < 0 || x >= H || v < 0 || v >= B) continue;
+    const int x = tok[j], v = slot[j], y = evicted[j], i = pos[j];
+    const bool ok = x >= 0 && x < H && v >= 0 && v < B;
+    lslot[j] = ok && i >= 0 && i < k ? v : -1;  // a row only for a sound entry
+    lpos[j] = i;
+    if (!ok) continue;
     if (y >= 0 && y < H) a.page[rH + y] = -1;
     a.page[rH + x] = v;
     a.slot_tok[rB + v] = x;
   }
-  const int row16 = a.row16, total = m * row16;
-  for (int c = tid; c < total; c += blockDim.x) {
-    const int j = c / row16, q = c - j * row16;
-    const int v = slot[j], i = pos[j];
-    if (v < 0 || v >= B || i < 0 || i >= k) continue;
-    a.hot[(rB + v) * row16 + q] = a.gather[(rk + i) * row16 + q];
+  __syncthreads();
+  // missed rows, gather output -> victim slots: the slot and position of a chunk come from LDS, so each
+  // thread keeps kUnroll 16-byte loads in flight with nothing between them
+  const int row16 = a.row16, total = m * row16, nt = blockDim.x;
+  for (int c0 = tid; c0 < total; c0 += nt * kUnroll) {
+    v4u val[kUnroll];
+    int64_t dst[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = c0 + u * nt;
+      dst[u] = -1;
+      if (c < total) {
+        const int j = c / row16, q = c - j * row16;
+        const int v = lslot[j];
+        if (v >= 0) {
+          val[u] = a.gather[(rk + lpos[j]) * row16 + q];
+          dst[u] = (int64_t)(rB + v) * row16 + q;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (dst[u] >= 0) a.hot[dst[u]] = val[u];
   }
   if (tid == 0) {
     a.step[r] = t + 1;
@@ -709,7 +732,8 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
 }
 
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(commit_kernel, dim3(a.R), dim3(1024), (size_t)a.B, s, a);
+  const size_t lds = (size_t)((a.B + 3) & ~3) + 8 * (size_t)a.k;  // flags, then slots and positions
+  hipLaunchKernelGGL(commit_kernel, dim3(a.R), dim3(1024), lds, s, a);
   return hipGetLastError();
 }
 
