@@ -164,6 +164,42 @@ def test_unfused_gather_against_oracle(k, B, H, T, rb):
     p.close()
 
 
+def test_maximum_request_count():
+    """65535 requests (the largest count, and the largest grid dimension the kernels use for it): fused resolve
+    with the gather, plan + copy with the gather, unfused gather and offload, every request against the oracle."""
+    import hierarchical_memory_amd as hm
+    rng = np.random.default_rng(65535)
+    R, k, B, H, rb, steps = 65535, 4, 8, 24, 16, 4
+    w = workload.SINGLE_4K.with_(name="max_requests", num_requests=R, top_k=k, buffer_slots=B, host_rows=H, L0=H,
+                                 row_elems=rb // 2, steps=steps, fused_gather=True)
+    ids = np.stack([np.stack([rng.choice(H, size=k, replace=False) for _ in range(steps)]) for _ in range(R)])
+    p = Pair(w, ids=ids.astype(np.int32), gather=True)
+    p.step(check_state=True)
+    out, miss, status, g = p.outs
+    plan = p.sw.plan_buffer()
+    topk = torch.from_numpy(np.ascontiguousarray(p.ids[:, 1])).cuda()
+    hm.hs_plan(p.sw.ctx, topk, None, out, miss, status, plan)
+    hm.hs_copy(p.sw.ctx, plan, miss, g)
+    o_out, o_miss, _, o_g = p.o.step(p.ids[:, 1], gather=True)
+    assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+    assert (g.cpu().numpy() == o_g).all()
+    p.t += 1
+    p.check_state()
+    g2 = torch.empty_like(g)
+    hm.hs_gather(p.sw.ctx, out, g2)
+    assert torch.equal(g2, g)
+    rows = rng.integers(0, 256, size=(R, 2, rb), dtype=np.uint8)
+    pos = rng.integers(0, H - 1, size=R).astype(np.int32)
+    st = torch.zeros(R, dtype=torch.int32, device="cuda")
+    hm.hs_offload(p.sw.ctx, torch.from_numpy(rows).cuda(), torch.from_numpy(pos).cuda(), st)
+    assert (st.cpu().numpy() == p.o.offload(rows, pos)).all()
+    torch.cuda.synchronize()
+    assert (p.sw.host_pool() == p.o.host).all()
+    for _ in range(2, steps):
+        p.step(check_state=True)
+    p.close()
+
+
 def test_buffer_equals_topk_and_whole_context():
     """B = k (every free slot shares the previous step's stamp) and B >= context (compulsory misses only)."""
     for B in (256, 4096):
