@@ -42,6 +42,7 @@ def _random_ids(rng, R, steps, k, H, extra_low=-3, extra_high=3, p_weird=0.1):
 TINY = [  # (k, B, H, T, row_bytes)
     (1, 1, 3, 0, 16), (2, 3, 6, 0, 16), (3, 4, 6, 0, 48), (3, 3, 5, 2, 16), (7, 9, 30, 0, 32),
     (12, 20, 40, 6, 16), (33, 40, 100, 0, 1152), (64, 64, 200, 0, 64), (65, 130, 257, 17, 80),
+    (2, 4, 6, 1, 1 << 20),  # the largest row: 1 MiB
 ]
 
 
@@ -139,6 +140,7 @@ GATHER_CASES = [  # (k, B, H, T, row_bytes); a workgroup of the gather covers ma
     (33, 40, 100, 0, 1152),  # 10 rows per workgroup: the last of 4 workgroups holds 3
     (65, 130, 257, 17, 80),  # 153 rows per workgroup: one partial workgroup; tail rows
     (5, 8, 20, 3, 16384),  # 1024 chunks per row: one row per workgroup in two passes, the second ragged
+    (2, 4, 6, 1, 1 << 20),  # the largest row: 65536 chunks, one row per workgroup in 86 passes
     (2048, 4096, 8192, 0, 1152),
 ]
 
@@ -386,6 +388,7 @@ COPY_GATHER_CASES = [  # (k, B, H, T, row_bytes, policy)
     (200, 330, 1500, 40, 80, 0),  # device tail
     (33, 40, 300, 7, 1152, 1),  # 10 rows per workgroup, the last of 4 holds 3; FIFO
     (5, 8, 60, 3, 16384, 0),  # 1024 chunks per row: one row per workgroup in two passes
+    (2, 4, 6, 1, 1 << 20, 1),  # the largest row (1 MiB); FIFO
 ]
 
 
