@@ -182,7 +182,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   // thread-contiguous chunks of bitmap words and of slots / order positions
   const int cw = (W + kThreads - 1) / kThreads, w0 = min(W, tid * cw), w1 = min(W, w0 + cw);
   const int cb = (B + kThreads - 1) / kThreads, s0 = min(B, tid * cb), s1 = min(B, s0 + cb);
-  auto resident = [&](int32_t x) { return has_tail && x >= t0 && (int64_t)x - (int64_t)t0 < (int64_t)T; };
+  // x - t0 is exact in uint32 once x >= t0, whatever the signs
+  auto resident = [&](int32_t x) { return has_tail && x >= t0 && (uint32_t)x - (uint32_t)t0 < (uint32_t)T; };
   int st = 0;
 
   // ---- phase 0: stage and classify, and build the selected and candidate bitmaps. The first round of every
@@ -213,37 +214,53 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     const int yy[4] = {y.x, y.y, y.z, y.w};
     const uint32_t oo[4] = {o.x & 0xffffu, o.x >> 16, o.y & 0xffffu, o.y >> 16};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) bad |= (yy[c] < -1 || yy[c] >= H || (int)oo[c] >= B);
+    for (int c = 0; c < 4; ++c) bad |= ((uint32_t)yy[c] + 1u > (uint32_t)H) | (oo[c] >= (uint32_t)B);  // y in [-1, H)
   };
+  // without branches: -1 is padding; outside [0, H), or at or past the tail start but outside the tail, is a
+  // bad id; inside the tail is resident; anything else is a candidate for the hot buffer
   auto classify = [&](int32_t x) -> int8_t {
-    if (x == -1) return C_PAD;
-    if (x < 0 || x >= H) { st |= kStatusBadId; return C_BAD; }
-    if (has_tail && x >= t0) {
-      if ((int64_t)x - (int64_t)t0 < (int64_t)T) return C_RES;
-      st |= kStatusBadId;
-      return C_BAD;
-    }
-    return C_CAND;
+    const bool past = has_tail && x >= t0;
+    const bool res = past && (uint32_t)x - (uint32_t)t0 < (uint32_t)T;
+    const bool badid = x != -1 && (x < 0 || x >= H || (past && !res));
+    st |= badid ? kStatusBadId : 0;
+    return x == -1 ? C_PAD : badid ? C_BAD : res ? C_RES : C_CAND;
   };
   // a selected id (candidate or resident) goes into the selected bitmap, a candidate also into the candidate
-  // bitmap; finding its bit already set means the selection repeats an id
+  // bitmap; finding its bit already set means the selection repeats an id. Without branches: an id that is
+  // not selected ORs nothing into word 0.
   auto mark = [&](int32_t x, int8_t c) {
-    if (c == C_CAND || c == C_RES) {
-      const uint32_t bit = 1u << (x & 31);
-      if (atomicOr(&sel[x >> 5], bit) & bit) repeat = 1;
-      if (c == C_CAND) atomicOr(&cbits[x >> 5], bit);
-    }
+    const bool s = c == C_CAND || c == C_RES;
+    const int wi = s ? (x >> 5) : 0;
+    const uint32_t bit = s ? 1u << (x & 31) : 0u;
+    const uint32_t old = atomicOr(&sel[wi], bit);
+    atomicOr(&cbits[wi], c == C_CAND ? bit : 0u);
+    repeat |= (old & bit) != 0u;
   };
   auto ids4 = [&](int i, int4 x) {
     reinterpret_cast<int4*>(ids)[i] = x;
     reinterpret_cast<int4*>(rank_slot)[i] = make_int4(-1, -1, -1, -1);
-    const int8_t cx = classify(x.x), cy = classify(x.y), cz = classify(x.z), cw = classify(x.w);
-    reinterpret_cast<uint32_t*>(cls)[i] = (uint32_t)(uint8_t)cx | ((uint32_t)(uint8_t)cy << 8) |
-                                          ((uint32_t)(uint8_t)cz << 16) | ((uint32_t)(uint8_t)cw << 24);
-    mark(x.x, cx);
-    mark(x.y, cy);
-    mark(x.z, cz);
-    mark(x.w, cw);
+    const int32_t xs[4] = {x.x, x.y, x.z, x.w};
+    int8_t c[4];
+    int wi[4];
+    uint32_t bit[4], old[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      c[u] = classify(xs[u]);
+      const bool s = c[u] == C_CAND || c[u] == C_RES;
+      wi[u] = s ? (xs[u] >> 5) : 0;
+      bit[u] = s ? 1u << (xs[u] & 31) : 0u;
+    }
+    reinterpret_cast<uint32_t*>(cls)[i] = (uint32_t)(uint8_t)c[0] | ((uint32_t)(uint8_t)c[1] << 8) |
+                                          ((uint32_t)(uint8_t)c[2] << 16) | ((uint32_t)(uint8_t)c[3] << 24);
+    // what mark does, for four ids at once: every atomic is issued before the first result is looked at
+#pragma unroll
+    for (int u = 0; u < 4; ++u) old[u] = atomicOr(&sel[wi[u]], bit[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) atomicOr(&cbits[wi[u]], c[u] == C_CAND ? bit[u] : 0u);
+    uint32_t rep = 0u;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rep |= old[u] & bit[u];
+    repeat |= rep != 0u;
   };
 
   if (tid < n4B) stage4(tid, y0, o0);
