@@ -59,7 +59,7 @@ constexpr int kUnroll = 4;  // 16-byte loads each thread keeps in flight in the 
 
 // misc words in LDS: one slot array of wave totals per block scan, then the status word
 constexpr int kMiscScanSel = 0, kMiscScanRank = kWaves, kMiscScanTail = 2 * kWaves, kMiscStatus = 3 * kWaves,
-              kMiscRepeat = 3 * kWaves + 1;
+              kMiscRepeat = 3 * kWaves + 1, kMiscBad = 3 * kWaves + 2;
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2, 4, 8 inside each row of 16
 // lanes, then the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).
@@ -74,18 +74,21 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 }
 
 // Exclusive prefix sum of one value per thread over the workgroup. sh: kWaves ints used by this call only.
+// After the exchange, lanes 0..15 of every wave hold the 16 wave totals and scan them in one DPP row; the
+// wave's offset and the block total are two lane reads of that row.
+static_assert(kWaves == 16, "the wave totals fill one DPP row");
 __device__ __forceinline__ int block_excl_scan(int v, int* sh, int lane, int wave, int* total) {
   const int inc = wave_incl_scan(v);
   if (lane == 63) sh[wave] = inc;
   __syncthreads();
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int w2 = 0; w2 < kWaves; ++w2) {
-    const int x = sh[w2];
-    tot += x;
-    pre += (w2 < wave) ? x : 0;
-  }
-  *total = tot;
+  int x = lane < kWaves ? sh[lane] : 0;
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  const int pre = w > 0 ? __builtin_amdgcn_readlane(x, w - 1) : 0;
+  *total = __builtin_amdgcn_readlane(x, kWaves - 1);
   return pre + inc - v;
 }
 
@@ -202,9 +205,13 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   uint2 o0 = make_uint2(0u, 0u);
   if (tid < n4B) { y0 = st4[tid]; o0 = or4[tid]; }
   if (tid < n4k) x0 = tk4[tid];
-  for (int w = tid; w < W; w += kThreads) { sel[w] = 0u; cbits[w] = 0u; hbits[w] = 0u; }
-  for (int i = tid; i < k; i += kThreads) first[i] = INT_MAX;
-  if (tid == 0) { misc[kMiscStatus] = 0; misc[kMiscRepeat] = 0; }
+  {
+    // the three bitmaps are adjacent, each padded to 16 bytes: cleared together in 16-byte stores
+    uint4* bm = reinterpret_cast<uint4*>(smem + L.sel);
+    const int n16 = (int)((L.selpre - L.sel) >> 4);
+    for (int q = tid; q < n16; q += kThreads) bm[q] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (tid == 0) { misc[kMiscStatus] = 0; misc[kMiscRepeat] = 0; misc[kMiscBad] = 0; }
   __syncthreads();
 
   auto stage4 = [&](int i, int4 y, uint2 o) {
@@ -287,9 +294,19 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       mark(x, c);
     }
   }
+  // one barrier publishes both flags (every writer stores the same 1)
   if (repeat) misc[kMiscRepeat] = 1;
-  bad = __syncthreads_or(bad);
+  if (bad) misc[kMiscBad] = 1;
+  __syncthreads();
+  bad = misc[kMiscBad];
   const bool repeats = misc[kMiscRepeat] != 0;  // rare: only then do positions bid for their id's rank
+  if (repeats && !bad) {
+    for (int i = tid; i < k; i += kThreads) first[i] = INT_MAX;
+    __syncthreads();
+  }
+  // a thread whose chunk is four whole slots (B = 4 x threads) reads its slot-table entries, order entries
+  // and slot flags with one LDS access each, 16-, 8- and 4-byte aligned
+  const bool whole4 = cb == 4 && s1 - s0 == 4;
 
   if (bad) {
     // impossible state: leave the request untouched
@@ -329,15 +346,23 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       if (repeats) atomicMin(&first[q], i);
     }
   }
-  for (int s = s0; s < s1; ++s) {
-    const int32_t y = stok[s];
-    if (y < 0 || resident(y)) continue;  // empty, or resident (a resident id takes no slot)
+  auto probe_slot = [&](int s, int32_t y) {
+    if (y < 0 || resident(y)) return;  // empty, or resident (a resident id takes no slot)
     const uint32_t word = sel[y >> 5];
     if (word & (1u << (y & 31))) {
       rank_slot[(int)selpre[y >> 5] + __popc(word & below(y))] = s;
       sflag[s] = 1;
       atomicOr(&hbits[y >> 5], 1u << (y & 31));
     }
+  };
+  if (whole4) {
+    const int4 y4 = *reinterpret_cast<const int4*>(stok + s0);
+    probe_slot(s0, y4.x);
+    probe_slot(s0 + 1, y4.y);
+    probe_slot(s0 + 2, y4.z);
+    probe_slot(s0 + 3, y4.w);
+  } else {
+    for (int s = s0; s < s1; ++s) probe_slot(s, stok[s]);
   }
   __syncthreads();
   // Repeats: a position that lost its rank's bid holds a repeated id. From here on a position's cls and rnk
@@ -363,7 +388,24 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   {
     int cm = 0, cc = 0;
     for (int w = w0; w < w1; ++w) cm += __popc(cbits[w] & ~hbits[w]);
-    for (int p = s0; p < s1; ++p) cc += !(sflag[ord[p]] & 1);
+    // a whole chunk keeps its four slots and their flags in registers for the victim pass below: no flag it
+    // reads there is written in between (each slot sits at one position of the order)
+    int sl4[4] = {0, 0, 0, 0};
+    uint32_t fl4[4] = {0u, 0u, 0u, 0u};
+    if (whole4) {
+      const uint2 o = *reinterpret_cast<const uint2*>(ord + s0);
+      sl4[0] = (int)(o.x & 0xffffu);
+      sl4[1] = (int)(o.x >> 16);
+      sl4[2] = (int)(o.y & 0xffffu);
+      sl4[3] = (int)(o.y >> 16);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        fl4[u] = sflag[sl4[u]];
+        cc += !(fl4[u] & 1u);
+      }
+    } else {
+      for (int p = s0; p < s1; ++p) cc += !(sflag[ord[p]] & 1);
+    }
     int tot;
     const int pre = block_excl_scan(cm | (cc << 16), misc + kMiscScanRank, lane, wave, &tot);
     m = tot & 0xffff;
@@ -388,11 +430,10 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     // LRU: the new order opens with the candidates that stay; FIFO: with every slot that stays (hits keep
     // their place), position p moving up by the number of victims before it
     int runC = (int)((uint32_t)pre >> 16);
-    for (int p = s0; p < s1; ++p) {
-      const int slot = ord[p];
-      if (sflag[slot] & 1) {
+    auto place = [&](int p, int slot, uint32_t flag) {
+      if (flag & 1u) {
         if (fifo) new_order[p - min(m, runC)] = (uint16_t)slot;
-        continue;
+        return;
       }
       if (runC < m) {
         vict[runC] = slot;
@@ -401,6 +442,15 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
         new_order[fifo ? p - m : runC - m] = (uint16_t)slot;
       }
       ++runC;
+    };
+    if (whole4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) place(s0 + u, sl4[u], fl4[u]);
+    } else {
+      for (int p = s0; p < s1; ++p) {
+        const int slot = ord[p];
+        place(p, slot, sflag[slot]);
+      }
     }
   }
   __syncthreads();
@@ -447,14 +497,29 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   // (FIFO); the scan's barrier also publishes the LDS writes above
   const int tail_start = fifo ? B - m : ncand - m;
   {
+    auto used = [&](uint32_t f) { return fifo ? f == 2u : f != 0u; };
     int ch = 0;
-    for (int s = s0; s < s1; ++s) ch += fifo ? sflag[s] == 2 : sflag[s] != 0;
+    uint32_t f4 = 0u;  // a whole chunk's four flags, one byte each
+    if (whole4) {
+      f4 = *reinterpret_cast<const uint32_t*>(sflag + s0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ch += used((f4 >> (8 * u)) & 0xffu);
+    } else {
+      for (int s = s0; s < s1; ++s) ch += used(sflag[s]);
+    }
     int tot;
     int pos = tail_start + block_excl_scan(ch, misc + kMiscScanTail, lane, wave, &tot);
-    for (int s = s0; s < s1; ++s) {
-      if (fifo ? sflag[s] != 2 : sflag[s] == 0) continue;
+    auto append = [&](int s) {
       if (pos < B) new_order[pos] = (uint16_t)s;  // pos < B always holds for a permutation
       ++pos;
+    };
+    if (whole4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (used((f4 >> (8 * u)) & 0xffu)) append(s0 + u);
+    } else {
+      for (int s = s0; s < s1; ++s)
+        if (used(sflag[s])) append(s);
     }
   }
   // stamps of hit and victim slots, and the victims' slot-table entries: consecutive lanes write
