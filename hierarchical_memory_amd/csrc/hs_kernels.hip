@@ -305,8 +305,27 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     __syncthreads();
   }
   // a thread whose chunk is four whole slots (B = 4 x threads) reads its slot-table entries, order entries
-  // and slot flags with one LDS access each, 16-, 8- and 4-byte aligned
+  // and slot flags with one LDS access each, 16-, 8- and 4-byte aligned; likewise a whole chunk of two or
+  // four bitmap words is one 8- or 16-byte access, its uint16 prefixes one 4- or 8-byte store
   const bool whole4 = cb == 4 && s1 - s0 == 4;
+  const bool wvec = (cw == 2 || cw == 4) && w1 - w0 == cw;
+  auto load_words = [&](const uint32_t* bm, uint32_t (&v)[4]) {
+    if (cw == 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(bm + w0);
+      v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    } else {
+      const uint2 q = *reinterpret_cast<const uint2*>(bm + w0);
+      v[0] = q.x; v[1] = q.y; v[2] = 0u; v[3] = 0u;
+    }
+  };
+  // prefixes of a whole chunk: run, then run plus the popcounts of the words before each
+  auto store_prefixes = [&](uint16_t* pre, const uint32_t (&v)[4], int run) {
+    const uint32_t p0 = (uint32_t)run, p1 = p0 + __popc(v[0]), p2 = p1 + __popc(v[1]), p3 = p2 + __popc(v[2]);
+    if (cw == 4)
+      *reinterpret_cast<uint2*>(pre + w0) = make_uint2((p0 & 0xffffu) | (p1 << 16), (p2 & 0xffffu) | (p3 << 16));
+    else
+      *reinterpret_cast<uint32_t*>(pre + w0) = (p0 & 0xffffu) | (p1 << 16);
+  };
 
   if (bad) {
     // impossible state: leave the request untouched
@@ -324,12 +343,22 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   // ---- phase 1: prefix counts of the selected bitmap (the rank of a selected id is one lookup)
   {
     int cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
+    uint32_t v[4] = {0u, 0u, 0u, 0u};
+    if (wvec) {
+      load_words(sel, v);
+      cnt = __popc(v[0]) + __popc(v[1]) + __popc(v[2]) + __popc(v[3]);
+    } else {
+      for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
+    }
     int n_sel;
     int run = block_excl_scan(cnt, misc + kMiscScanSel, lane, wave, &n_sel);
-    for (int w = w0; w < w1; ++w) {
-      selpre[w] = (uint16_t)run;
-      run += __popc(sel[w]);
+    if (wvec) {
+      store_prefixes(selpre, v, run);
+    } else {
+      for (int w = w0; w < w1; ++w) {
+        selpre[w] = (uint16_t)run;
+        run += __popc(sel[w]);
+      }
     }
   }
   __syncthreads();
@@ -387,7 +416,19 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   int m, ncand;
   {
     int cm = 0, cc = 0;
-    for (int w = w0; w < w1; ++w) cm += __popc(cbits[w] & ~hbits[w]);
+    uint32_t mw[4] = {0u, 0u, 0u, 0u};  // a whole chunk's missed-id words, kept for the prefixes below
+    if (wvec) {
+      uint32_t hw[4];
+      load_words(cbits, mw);
+      load_words(hbits, hw);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        mw[u] &= ~hw[u];
+        cm += __popc(mw[u]);
+      }
+    } else {
+      for (int w = w0; w < w1; ++w) cm += __popc(cbits[w] & ~hbits[w]);
+    }
     // a whole chunk keeps its four slots and their flags in registers for the victim pass below: no flag it
     // reads there is written in between (each slot sits at one position of the order)
     int sl4[4] = {0, 0, 0, 0};
@@ -423,9 +464,13 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       return;
     }
     int run = pre & 0xffff;
-    for (int w = w0; w < w1; ++w) {
-      mpre[w] = (uint16_t)run;
-      run += __popc(cbits[w] & ~hbits[w]);
+    if (wvec) {
+      store_prefixes(mpre, mw, run);
+    } else {
+      for (int w = w0; w < w1; ++w) {
+        mpre[w] = (uint16_t)run;
+        run += __popc(cbits[w] & ~hbits[w]);
+      }
     }
     // LRU: the new order opens with the candidates that stay; FIFO: with every slot that stays (hits keep
     // their place), position p moving up by the number of victims before it
