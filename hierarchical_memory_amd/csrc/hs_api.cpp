@@ -78,7 +78,7 @@ int check_config(const hs_config* cfg, int32_t* H_out, hs::Layout* L_out) {
                 cfg->num_requests, (long long)H, cfg->row_bytes);
   const hs::Layout L = hs::make_layout(cfg->top_k, cfg->device_buffer_size, (int)H);
   // 1 KiB of the 160 KiB of a gfx950 compute unit stays for the kernel's static LDS
-  if (L.total > 159u * 1024u)
+  if (L.total > hs::kLdsCap)
     return fail(HS_E_INVALID,
                 "this shape needs %u bytes of LDS per workgroup (top_k %d, buffer %d, host rows %lld), "
                 "more than the 159 KiB one resolve workgroup may use on gfx950",
@@ -168,7 +168,7 @@ int hs_create(const hs_config* cfg, hs_ctx** out) {
                 lds_max);
   // The cap on dynamic LDS is an attribute of the kernels, shared by every context on the device: set it to
   // the most any context may use, so a later context of a smaller shape cannot lower it under this one.
-  const uint32_t cap = std::min<uint32_t>(159u * 1024u, (uint32_t)lds_max - 1024u);
+  const uint32_t cap = std::min<uint32_t>(hs::kLdsCap, (uint32_t)lds_max - 1024u);
   e = hs::set_lds_limits(cap, cap);
   if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(resolve kernel LDS)");
 

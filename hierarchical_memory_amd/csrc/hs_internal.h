@@ -8,6 +8,7 @@ namespace hs {
 
 constexpr int kThreads = 1024;            // resolve workgroup: 16 wave64s
 constexpr int kWaves = kThreads / 64;
+constexpr uint32_t kLdsCap = 159u * 1024u;  // LDS one resolve workgroup may use (gfx950 has 160 KiB per CU)
 constexpr int kMaxTopK = 8192;
 constexpr int kMaxSlots = 65535;          // slot ids fit the uint16 LRU order list
 
@@ -46,9 +47,13 @@ inline Layout make_layout(int k, int B, int H) {
   L.first = take(4ull * k);
   L.mpre = L.selpre;
   L.vict = L.first;
-  L.mtok = L.rank_slot;  // rank -> hit slot is dead once each position has taken its slot
   L.gsrc = take(4ull * k);
   L.misc = take(4ull * (4 * kWaves + 8));
+  // The missed tokens get an array of their own when it still fits: then a selection without repeated ids
+  // reads each hit slot from rank_slot while pairing, with no pass of its own. Otherwise they reuse rank_slot,
+  // dead once every position has taken its slot in that pass.
+  if (align16(off + 4ull * k) <= kLdsCap) L.mtok = take(4ull * k);
+  else L.mtok = L.rank_slot;
   L.total = (uint32_t)off;
   return L;
 }

@@ -397,7 +397,10 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   // Repeats: a position that lost its rank's bid holds a repeated id. From here on a position's cls and rnk
   // entries are read and written by its own thread only, so rnk takes the position's slot (hit) or -1, and
   // phase 3 needs no barrier before it: it reads bitmaps, slot flags and the order list, final above.
-  for (int i = tid; i < k; i += kThreads) {
+  // Without repeats, and with the missed tokens in an array of their own (rank_slot then lives through the
+  // pairing), this pass is left to the pairing, which reads the hit slot under the position's rank.
+  const bool settle = repeats || L.mtok == L.rank_slot;
+  for (int i = tid; settle && i < k; i += kThreads) {
     const int8_t c = cls[i];
     if (c == C_CAND || c == C_RES) {
       const int q = rnk[i];
@@ -507,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     const int32_t x = ids[i];
     int32_t o = -1, g = -1;
     const bool cand = c == C_CAND;
-    const int32_t hit = cand ? rnk[i] : -1;
+    const int32_t hit = cand ? (settle ? rnk[i] : rank_slot[rnk[i]]) : -1;
     if (cand && hit < 0) {  // a miss
       const int w = x >> 5;
       const int j = (int)mpre[w] + __popc(cbits[w] & ~hbits[w] & below(x));
