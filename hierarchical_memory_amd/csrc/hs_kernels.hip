@@ -808,11 +808,20 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   const uint16_t* nord = reinterpret_cast<const uint16_t*>(rec + kTrialHead + 4 * k);
   for (int s = tid; s < B; s += blockDim.x) used[s] = 0;
   __syncthreads();
-  for (int p = tid; p < B; p += blockDim.x) {
-    const int o = nord[p];
-    if (o >= B) continue;  // only a corrupt record
-    a.order[rB + p] = (uint16_t)o;
-    if (p >= u0) used[o] = 1;
+  // four strided entries per thread at a time, all loaded before any is stored: the record and the order
+  // list are both global memory, so a store could otherwise hold back the next entry's load
+  const int nt = blockDim.x;
+  for (int p0 = tid; p0 < B; p0 += 4 * nt) {
+    int o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = p0 + u * nt < B ? nord[p0 + u * nt] : B;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + u * nt;
+      if (p >= B || o[u] >= B) continue;  // past the end, or a corrupt record
+      a.order[rB + p] = (uint16_t)o[u];
+      if (p >= u0) used[o[u]] = 1;
+    }
   }
   __syncthreads();
   for (int s = tid; s < B; s += blockDim.x)
@@ -834,7 +843,7 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   __syncthreads();
   // missed rows, gather output -> victim slots: the slot and position of a chunk come from LDS, so each
   // thread keeps kUnroll 16-byte loads in flight with nothing between them
-  const int row16 = a.row16, total = m * row16, nt = blockDim.x;
+  const int row16 = a.row16, total = m * row16;
   for (int c0 = tid; c0 < total; c0 += nt * kUnroll) {
     v4u val[kUnroll];
     int64_t dst[kUnroll];
