@@ -70,7 +70,7 @@ extern "C" {
  * Hierarchical Memory", section 3 launch scripts: top_k 2048,
  * device_buffer_size 4096 or 6144, host_to_device_ratio 8 or 10).
  * Beyond the per-field ranges, a shape is accepted only if one resolve
- * workgroup's LDS (hs_sizes.lds_bytes, about 25k + 7B + 14 * ceil(H / 32)
+ * workgroup's LDS (hs_sizes.lds_bytes, about 21k + 7B + 14 * ceil(H / 32)
  * bytes, plus 4k more where that still fits, which saves the kernel a pass)
  * fits in 159 KiB, and the host pool (R x H x row_bytes) in 2^56 bytes;
  * hs_required_sizes and hs_create return HS_E_INVALID otherwise.

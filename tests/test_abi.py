@@ -94,6 +94,25 @@ def test_sizes_of_the_workloads():
         assert s.hot_bytes == w.num_requests * w.buffer_slots * w.row_bytes
 
 
+def test_lds_layout_takes_the_missed_token_array_where_it_fits():
+    """One resolve workgroup needs about 21k + 7B + 14 ceil(H/32) bytes of LDS; the missed tokens get 4k bytes
+    of their own only while the total stays within 159 KiB (near the limit they share the rank-to-slot table)."""
+    def base(k, B, H):
+        return 21 * k + 7 * B + 14 * ((H + 31) // 32)
+
+    def lds(k, B, H):
+        return hm.hs_required_sizes(hm.config(2, k, B, 0.0, 1152, H)).lds_bytes
+
+    for k, B, H in ((2048, 4096, 40960), (2048, 4096, 131072), (256, 512, 4096), (2048, 8192, 120000)):
+        extra = lds(k, B, H) - base(k, B, H)
+        assert 4 * k <= extra <= 4 * k + 512, (k, B, H, extra)
+        assert lds(k, B, H) <= 159 * 1024
+    for k, B, H in ((2048, 8192, 131072), (4096, 4096, 100000)):
+        extra = lds(k, B, H) - base(k, B, H)
+        assert 0 <= extra <= 512, (k, B, H, extra)
+        assert lds(k, B, H) + 4 * k > 159 * 1024
+
+
 def test_binding_refuses_host_tensors():
     """Per-call buffers must be GPU tensors: a CPU tensor is refused before anything reaches the library."""
     import torch

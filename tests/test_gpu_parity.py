@@ -351,6 +351,36 @@ def test_largest_shape_that_fits_lds():
     p.close()
 
 
+def test_shared_missed_token_array_near_the_lds_limit():
+    """At k = 2048, B = 8192, H = 131072 a separate missed-token array would pass 159 KiB of LDS, so the missed
+    tokens share the rank-to-slot table and the kernel keeps its settling pass: steps without and with repeated
+    ids, fused and through plan + copy."""
+    import hierarchical_memory_amd as hm
+    s = hm.hs_required_sizes(hm.config(2, 2048, 8192, 0.0, 1152, 131072))
+    assert s.lds_bytes + 4 * 2048 > 159 * 1024
+    w = workload.SINGLE_4K.with_(name="wide_shared", num_requests=2, top_k=2048, buffer_slots=8192,
+                                 host_rows=131072, L0=131072, window=20000, steps=8)
+    ids = workload.streams(w)
+    ids[:, 1::2, 7] = ids[:, 1::2, 3]  # odd steps repeat an id
+    p = Pair(w, ids=ids)
+    p.run(check_every=1)
+    p.close()
+    p = Pair(w, ids=ids)
+    plan = p.sw.plan_buffer()
+    out, miss, status, _ = p.outs
+    for t in range(w.steps):
+        step_ids = p.ids[:, t]
+        hm.hs_plan(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(step_ids)).cuda(), None, out, miss, status, plan)
+        hm.hs_copy(p.sw.ctx, plan, miss)
+        o_out, o_miss, o_status, _ = p.o.step(step_ids[p.sample])
+        s = p.sample_t
+        assert (out[s].cpu().numpy() == o_out).all() and (miss[s].cpu().numpy() == o_miss).all()
+        assert (status[s].cpu().numpy() == o_status).all()
+        p.t += 1
+        p.check_state()
+    p.close()
+
+
 def _check_plan(plan_r, out_r, ids_r, m):
     """The plan lists the step's missed ids in ascending order with the slots they were given."""
     toks = plan_r[0][:m]
