@@ -94,6 +94,13 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int lane, int wav
 
 __device__ __forceinline__ uint32_t below(int32_t x) { return (1u << (x & 31)) - 1u; }
 
+// Element i of an array whose byte size stays below 4 GiB (per-request rows of k or B entries): the byte
+// offset is formed in 32 bits, so a store takes the scalar-base + 32-bit-offset form.
+template <class T>
+__device__ __forceinline__ T& at(T* base, uint32_t i) {
+  return *reinterpret_cast<T*>(reinterpret_cast<char*>(base) + i * (uint32_t)sizeof(T));
+}
+
 __device__ __forceinline__ v4u load_host(const v4u* p) { return __builtin_nontemporal_load(p); }
 
 // Missed rows from the host pool into their slots, flattened over (miss, 16-byte chunk): thread tid of nt
@@ -182,6 +189,13 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   const int32_t t0 = has_tail ? a.tail0[r] : 0;
   const int32_t t = a.step[r];
   const size_t rk = (size_t)r * k, rB = (size_t)r * B, rH = (size_t)r * H;
+  // per-request bases (uniform): with at(), stores take the scalar-base form with no 64-bit address arithmetic
+  // per lane
+  int32_t* const out_r = a.out + rk;
+  int32_t* const page_r = a.page + rH;
+  int32_t* const stamp_r = a.stamp + rB;
+  int32_t* const slot_tok_r = a.slot_tok + rB;
+  int32_t* const plan_r = a.plan + 3 * rk;  // used by plan launches only
   // thread-contiguous chunks of bitmap words and of slots / order positions
   const int cw = (W + kThreads - 1) / kThreads, w0 = min(W, tid * cw), w1 = min(W, w0 + cw);
   const int cb = (B + kThreads - 1) / kThreads, s0 = min(B, tid * cb), s1 = min(B, s0 + cb);
@@ -480,14 +494,14 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     int runC = (int)((uint32_t)pre >> 16);
     auto place = [&](int p, int slot, uint32_t flag) {
       if (flag & 1u) {
-        if (fifo) new_order[p - min(m, runC)] = (uint16_t)slot;
+        if (fifo) at(new_order, p - min(m, runC)) = (uint16_t)slot;
         return;
       }
       if (runC < m) {
         vict[runC] = slot;
         sflag[slot] = 2;
       } else {
-        new_order[fifo ? p - m : runC - m] = (uint16_t)slot;
+        at(new_order, fifo ? p - m : runC - m) = (uint16_t)slot;
       }
       ++runC;
     };
@@ -523,8 +537,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
         rec[kTrialHead + 2 * k + j] = y;
         rec[kTrialHead + 3 * k + j] = i;
       } else {
-        if (y >= 0) a.page[rH + y] = -1;
-        a.page[rH + x] = v;
+        if (y >= 0) page_r[y] = -1;  // H rows may pass 4 GiB of page table: 64-bit offsets here
+        page_r[x] = v;
       }
       stok[v] = x;
       mtok[j] = x;
@@ -537,9 +551,9 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       o = B + x % T;  // the tail is a ring: token x in row x mod T
       g = o;
     }
-    a.out[rk + i] = o;
+    at(out_r, i) = o;
     gsrc[i] = g;
-    if (kMode == kPlan) a.plan[rk * 3 + 2 * k + i] = g;  // where position i's row comes from (hs_copy's gather)
+    if (kMode == kPlan) at(plan_r, 2 * k + i) = g;  // where position i's row comes from (hs_copy's gather)
   }
   // the slots used this step close the new order in slot order: hits and victims (LRU) or victims only
   // (FIFO); the scan's barrier also publishes the LDS writes above
@@ -558,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     int tot;
     int pos = tail_start + block_excl_scan(ch, misc + kMiscScanTail, lane, wave, &tot);
     auto append = [&](int s) {
-      if (pos < B) new_order[pos] = (uint16_t)s;  // pos < B always holds for a permutation
+      if (pos < B) at(new_order, pos) = (uint16_t)s;  // pos < B always holds for a permutation
       ++pos;
     };
     if (whole4) {
@@ -575,15 +589,15 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   if (kMode != kTrial) {
     for (int s = tid; s < B; s += kThreads) {
       const uint8_t f = sflag[s];
-      if (fifo ? f == 2 : f != 0) a.stamp[rB + s] = t;
-      if (f == 2) a.slot_tok[rB + s] = stok[s];
+      if (fifo ? f == 2 : f != 0) at(stamp_r, s) = t;
+      if (f == 2) at(slot_tok_r, s) = stok[s];
     }
   }
 
   if (kMode == kPlan) {
     for (int j = tid; j < m; j += kThreads) {
-      a.plan[rk * 3 + j] = mtok[j];
-      a.plan[rk * 3 + k + j] = vict[j];
+      at(plan_r, j) = mtok[j];
+      at(plan_r, k + j) = vict[j];
     }
     if (tid == 0) {
       a.step[r] = t + 1;
