@@ -32,8 +32,9 @@
 //            mapped pinned host memory into the HBM slots (and every selected
 //            row into the gather output when fused).
 // Scans run over thread-contiguous chunks: a DPP scan inside each wave, one
-// exchange of the 16 wave totals through LDS. No result depends on the order of
-// LDS atomics (they are OR and MIN only).
+// exchange of the 16 wave totals through LDS, which each wave scans again in
+// one DPP row. No result depends on the order of LDS atomics (they are OR and
+// MIN only).
 //
 // The LRU order list keeps each request's slots sorted by (stamp, slot). After
 // a step, the non-victim candidates keep their stamps and relative order, and
@@ -943,6 +944,8 @@ __global__ __launch_bounds__(1024) void advance_tail_kernel(AdvanceTailArgs a) {
   v4u* hostr = a.host + rH * row16;
   v4u* hotr = a.hot + rB * row16;
   int skipped = 0;
+  // the ring row of token t0 + j is (t0 mod T) + j, wrapped once (j < n <= T)
+  const int t0m = (int)((((int64_t)t0 % T) + T) % T);
   for (int c = tid; c < n * row16; c += blockDim.x) {
     const int j = c / row16, q = c - j * row16;
     const int64_t x = (int64_t)t0 + j;
@@ -950,7 +953,9 @@ __global__ __launch_bounds__(1024) void advance_tail_kernel(AdvanceTailArgs a) {
       skipped = 1;
       continue;
     }
-    const v4u v = tailr[(size_t)(x % T) * row16 + q];
+    const uint32_t e = (uint32_t)t0m + (uint32_t)j;  // < 2T, exact in uint32
+    const uint32_t ring = e >= (uint32_t)T ? e - (uint32_t)T : e;
+    const v4u v = tailr[(size_t)ring * row16 + q];
     hostr[(size_t)x * row16 + q] = v;  // plain stores: non-temporal ones to host memory run ~10 % slower
     const int s = a.page[rH + x];
     if (s >= 0 && s < a.B) hotr[(size_t)s * row16 + q] = v;
