@@ -121,3 +121,17 @@ def test_binding_refuses_host_tensors():
         hm.hs_resolve(None, cpu, None, cpu, cpu, cpu)
     with pytest.raises(ValueError, match="GPU tensor"):
         hm.hs_gather(None, cpu, cpu)
+
+
+def test_build_script_loads_without_the_built_library():
+    """build() must work on a fresh checkout: loading the build script may not import the package, whose import
+    needs the library that the script is about to build."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys, os, __graft_entry__ as g; "
+            "m = g._load_by_path('_hs_build', os.path.join(g.ROOT, 'hierarchical_memory_amd', 'build.py')); "
+            "assert callable(m.build); "
+            "assert 'hierarchical_memory_amd' not in sys.modules, 'the package was imported'")
+    res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
