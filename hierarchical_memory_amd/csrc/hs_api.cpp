@@ -13,7 +13,9 @@
 struct hs_ctx {
   hs_config cfg;
   int32_t H;             // host rows per request
-  hs::Layout layout;
+  hs::Layout layout;          // the rank layout: what a context of this shape needs at least
+  hs::Layout layout_plain;    // launches without a gather output: the direct layout where it fits
+  hs::Layout layout_gather;   // launches with one (fused gather, trial)
   int device;
   void* pool_host;       // pinned, mapped host pool
   void* pool_dev;        // its device address
@@ -177,6 +179,8 @@ int hs_create(const hs_config* cfg, hs_ctx** out) {
   ctx->cfg = *cfg;
   ctx->H = H;
   ctx->layout = L;
+  ctx->layout_plain = hs::make_direct_layout(cfg->top_k, cfg->device_buffer_size, (int)H, false, cap);
+  ctx->layout_gather = hs::make_direct_layout(cfg->top_k, cfg->device_buffer_size, (int)H, true, cap);
   ctx->device = dev;
   ctx->pool_bytes = (uint64_t)cfg->num_requests * (uint64_t)H * (uint64_t)cfg->row_bytes;
   // Pinned host memory mapped into the GPU's address space; the resolve kernel reads missed rows
@@ -301,7 +305,7 @@ int resolve_common(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, i
     const int u = (per_request + hs::kThreads - 1) / hs::kThreads;
     a.copy_unroll = u <= 1 ? 1 : u == 2 ? 2 : 4;
   }
-  a.L = ctx->layout;
+  a.L = d_gather ? ctx->layout_gather : ctx->layout_plain;
   a.host = (const hs::v4u*)ctx->pool_dev;
   a.hot = (hs::v4u*)ctx->views.hot;
   a.tail = (const hs::v4u*)ctx->views.tail;

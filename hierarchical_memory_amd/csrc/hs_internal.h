@@ -22,7 +22,10 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte ch
 struct Layout {
   uint32_t ids, cls, rank_slot, rank, stok, ord, sflag, sel, cbits, hbits, selpre, first, mpre, vict, mtok, gsrc,
       misc;
-  uint32_t words;  // bitmap words = ceil(H / 32)
+  uint32_t bm_end;  // end of the three bitmaps (sel, cbits, hbits are adjacent and cleared together)
+  uint32_t t2s;     // token -> slot table (uint16 per host row) of the direct layout
+  uint32_t direct;  // 1: direct layout (t2s valid; rank_slot, rank, first and selpre live inside it)
+  uint32_t words;   // bitmap words = ceil(H / 32)
   uint32_t total;
 };
 
@@ -43,6 +46,7 @@ inline Layout make_layout(int k, int B, int H) {
   L.sel = take(4ull * L.words);     // selected ids (candidates and resident)
   L.cbits = take(4ull * L.words);   // candidate ids (not resident)
   L.hbits = take(4ull * L.words);   // candidate ids found in a slot
+  L.bm_end = (uint32_t)off;
   L.selpre = take(2ull * L.words);  // uint16 prefix counts (k <= 8192)
   L.first = take(4ull * k);
   L.mpre = L.selpre;
@@ -55,6 +59,47 @@ inline Layout make_layout(int k, int B, int H) {
   if (align16(off + 4ull * k) <= kLdsCap) L.mtok = take(4ull * k);
   else L.mtok = L.rank_slot;
   L.total = (uint32_t)off;
+  return L;
+}
+
+// The direct layout, where it fits in cap bytes (else the layout above): every host row of the request has a
+// uint16 entry in a token -> slot table, so a slot holding a selected token writes its index under the token
+// itself and the selected ids need no ranks. Nothing reads an entry whose token has no hit bit, so the table
+// is never cleared. A launch whose selection repeats an id still ranks (the lowest position holding an id
+// keeps it): the rank arrays and the selected set's prefix counts then live inside the table's region, which
+// that launch does not use otherwise. The miss prefixes, the victim list and the missed tokens get arrays of
+// their own; the per-position row sources only when the launch gathers rows.
+inline Layout make_direct_layout(int k, int B, int H, bool gather, uint64_t cap) {
+  Layout L{};
+  L.words = (uint32_t)(((uint64_t)H + 31) / 32);
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) { uint32_t o = (uint32_t)off; off = align16(off + bytes); return o; };
+  L.ids = take(4ull * k);
+  L.cls = take(1ull * k);
+  L.stok = take(4ull * B);
+  L.ord = take(2ull * B);
+  L.sflag = take(1ull * B);
+  L.sel = take(4ull * L.words);
+  L.cbits = take(4ull * L.words);
+  L.hbits = take(4ull * L.words);
+  L.bm_end = (uint32_t)off;
+  L.mpre = take(2ull * L.words);
+  L.vict = take(4ull * k);
+  L.mtok = take(4ull * k);
+  L.gsrc = gather ? take(4ull * k) : 0u;  // unused without a gather (a plan launch writes the sources out)
+  L.misc = take(4ull * (4 * kWaves + 8));
+  // the table's region, with the rank path's arrays inside it
+  const uint64_t region = off;
+  L.t2s = (uint32_t)region;
+  L.rank_slot = take(4ull * k);
+  L.rank = take(4ull * k);
+  L.first = take(4ull * k);
+  L.selpre = take(2ull * L.words);
+  const uint64_t table = align16(2ull * (uint64_t)H);
+  if (off < region + table) off = region + table;
+  L.total = (uint32_t)off;
+  L.direct = 1u;
+  if (off > cap) return make_layout(k, B, H);
   return L;
 }
 

@@ -13,7 +13,10 @@
 //            into LDS bitmaps over token ids: the selected set, and the
 //            candidates among it (not resident);
 //   phase 1  popcount prefix over the selected bitmap's words, so the rank of a
-//            selected id among the selected ids is one lookup;
+//            selected id among the selected ids is one lookup (skipped where the
+//            LDS holds a token -> slot table for every host row of the request,
+//            and the selection repeats no id: a hit slot then writes its index
+//            under its token, and a position reads it there);
 //   phase 2  in one pass, every selected position takes its id's rank and, when
 //            phase 0 saw an id twice, bids for it (the lowest position wins, so a
 //            repeated id is resolved without any order-dependent atomic) while
@@ -175,6 +178,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   int32_t* vict = (int32_t*)(smem + L.vict);
   int32_t* mtok = (int32_t*)(smem + L.mtok);
   int32_t* gsrc = (int32_t*)(smem + L.gsrc);
+  uint16_t* t2s = (uint16_t*)(smem + L.t2s);         // direct layout: token -> slot that holds it (hit)
   int32_t* misc = (int32_t*)(smem + L.misc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -223,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   {
     // the three bitmaps are adjacent, each padded to 16 bytes: cleared together in 16-byte stores
     uint4* bm = reinterpret_cast<uint4*>(smem + L.sel);
-    const int n16 = (int)((L.selpre - L.sel) >> 4);
+    const int n16 = (int)((L.bm_end - L.sel) >> 4);
     for (int q = tid; q < n16; q += kThreads) bm[q] = make_uint4(0u, 0u, 0u, 0u);
   }
   if (tid == 0) { misc[kMiscStatus] = 0; misc[kMiscRepeat] = 0; misc[kMiscBad] = 0; }
@@ -315,6 +319,9 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   __syncthreads();
   bad = misc[kMiscBad];
   const bool repeats = misc[kMiscRepeat] != 0;  // rare: only then do positions bid for their id's rank
+  // direct: a hit slot writes its index under its token in t2s, and no selected id needs a rank (phase 1 and
+  // the per-position half of phase 2 drop out); a selection that repeats an id ranks as below
+  const bool direct = L.direct != 0u && !repeats;
   if (repeats && !bad) {
     for (int i = tid; i < k; i += kThreads) first[i] = INT_MAX;
     __syncthreads();
@@ -356,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   }
 
   // ---- phase 1: prefix counts of the selected bitmap (the rank of a selected id is one lookup)
-  {
+  if (!direct) {
     int cnt = 0;
     uint32_t v[4] = {0u, 0u, 0u, 0u};
     if (wvec) {
@@ -375,13 +382,14 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
         run += __popc(sel[w]);
       }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // ---- phase 2: ranks and the hit test in one pass. Every selected position records the rank of its id and,
   // if the selection repeats an id, bids for it (the lowest position holding an id wins); every slot whose
-  // token is selected records itself under that token's rank and marks the token hit.
-  for (int i = tid; i < k; i += kThreads) {
+  // token is selected records itself under that token's rank (direct: under the token) and marks the token
+  // hit.
+  for (int i = tid; !direct && i < k; i += kThreads) {
     const int8_t c = cls[i];
     if (c == C_CAND || c == C_RES) {
       const int32_t x = ids[i];
@@ -394,7 +402,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     if (y < 0 || resident(y)) return;  // empty, or resident (a resident id takes no slot)
     const uint32_t word = sel[y >> 5];
     if (word & (1u << (y & 31))) {
-      rank_slot[(int)selpre[y >> 5] + __popc(word & below(y))] = s;
+      if (direct) t2s[y] = (uint16_t)s;
+      else rank_slot[(int)selpre[y >> 5] + __popc(word & below(y))] = s;
       sflag[s] = 1;
       atomicOr(&hbits[y >> 5], 1u << (y & 31));
     }
@@ -525,10 +534,20 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     const int32_t x = ids[i];
     int32_t o = -1, g = -1;
     const bool cand = c == C_CAND;
-    const int32_t hit = cand ? (settle ? rnk[i] : rank_slot[rnk[i]]) : -1;
+    const int w = x >> 5;
+    uint32_t hw = 0u;
+    int32_t hit = -1;
+    if (cand) {
+      if (direct) {
+        hw = hbits[w];
+        hit = (hw >> (x & 31)) & 1u ? (int32_t)t2s[x] : -1;
+      } else {
+        hit = settle ? rnk[i] : rank_slot[rnk[i]];
+      }
+    }
     if (cand && hit < 0) {  // a miss
-      const int w = x >> 5;
-      const int j = (int)mpre[w] + __popc(cbits[w] & ~hbits[w] & below(x));
+      if (!direct) hw = hbits[w];
+      const int j = (int)mpre[w] + __popc(cbits[w] & ~hw & below(x));
       const int v = vict[j];
       const int32_t y = stok[v];  // each victim belongs to exactly one miss
       if (kMode == kTrial) {
@@ -553,7 +572,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       g = o;
     }
     at(out_r, i) = o;
-    gsrc[i] = g;
+    if (kMode != kPlan && a.gather != nullptr) gsrc[i] = g;  // read by the gather below
     if (kMode == kPlan) at(plan_r, 2 * k + i) = g;  // where position i's row comes from (hs_copy's gather)
   }
   // the slots used this step close the new order in slot order: hits and victims (LRU) or victims only

@@ -73,7 +73,11 @@ extern "C" {
  * workgroup's LDS (hs_sizes.lds_bytes, about 21k + 7B + 14 * ceil(H / 32)
  * bytes, plus 4k more where that still fits, which saves the kernel a pass)
  * fits in 159 KiB, and the host pool (R x H x row_bytes) in 2^56 bytes;
- * hs_required_sizes and hs_create return HS_E_INVALID otherwise.
+ * hs_required_sizes and hs_create return HS_E_INVALID otherwise. Where a
+ * uint16 token -> slot entry for each of the H host rows fits beside the
+ * rest (about 13k + 7B + 14 * ceil(H / 32) + 2H bytes, 4k more for a launch
+ * with a gather output), a launch uses that larger layout, up to 159 KiB,
+ * and skips ranking the selected ids.
  */
 typedef struct hs_config {
   int32_t num_requests;       /* R, 1 .. 65535 */
@@ -120,7 +124,7 @@ typedef struct hs_sizes {
   uint64_t gather_bytes;     /* [R][k][row_bytes] gather output */
   uint64_t plan_bytes;       /* [R][3][k] int32 plan of hs_plan (miss list and row sources) */
   uint64_t trial_bytes;      /* trial records of hs_trial / hs_commit */
-  uint32_t lds_bytes;        /* LDS one resolve workgroup uses */
+  uint32_t lds_bytes;        /* LDS one resolve workgroup needs at least */
 } hs_sizes;
 
 typedef struct hs_ctx hs_ctx;

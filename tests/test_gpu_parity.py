@@ -381,6 +381,38 @@ def test_shared_missed_token_array_near_the_lds_limit():
     p.close()
 
 
+def test_token_slot_table_beside_the_rank_path():
+    """At the 256-request shape (k = 2048, B = 4096, H = 40960) a launch without a gather output has LDS for a
+    token -> slot entry per host row, so hit slots write their index under their token and the selected ids are
+    not ranked; a request whose selection repeats an id ranks them instead, in the same launch. With a gather
+    output the table does not fit and every request ranks. Requests 1 and 3 repeat an id on odd steps; fused
+    without and with a gather, and plan + copy, step by step against the oracle."""
+    import hierarchical_memory_amd as hm
+    w = workload.CONC_256.with_(name="conc_shape_4req", num_requests=4, steps=8)
+    ids = workload.streams(w)
+    ids[1, 1::2, 7] = ids[1, 1::2, 3]
+    ids[3, 1::2, 100] = ids[3, 1::2, 2000]
+    for gather in (False, True):
+        p = Pair(w, ids=ids, gather=gather)
+        p.run(check_every=1)
+        assert (p.outs[2].cpu().numpy()[[1, 3]] != 0).any(), "the repeated ids were not reported"
+        p.close()
+    p = Pair(w, ids=ids)
+    plan = p.sw.plan_buffer()
+    out, miss, status, _ = p.outs
+    for t in range(w.steps):
+        step_ids = p.ids[:, t]
+        hm.hs_plan(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(step_ids)).cuda(), None, out, miss, status, plan)
+        hm.hs_copy(p.sw.ctx, plan, miss)
+        o_out, o_miss, o_status, _ = p.o.step(step_ids[p.sample])
+        s = p.sample_t
+        assert (out[s].cpu().numpy() == o_out).all() and (miss[s].cpu().numpy() == o_miss).all()
+        assert (status[s].cpu().numpy() == o_status).all()
+        p.t += 1
+        p.check_state()
+    p.close()
+
+
 def _check_plan(plan_r, out_r, ids_r, m):
     """The plan lists the step's missed ids in ascending order with the slots they were given."""
     toks = plan_r[0][:m]
