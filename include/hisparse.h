@@ -103,6 +103,10 @@ typedef struct hs_config {
  * Device buffers (caller-owned). Sizes are in bytes and must be at least what
  * hs_required_sizes reports; pointers must be 16-byte aligned (hot, tail,
  * gather output) or 4-byte aligned (tables). H = host rows per request.
+ * The tables are written by the library; a caller that writes them (restoring
+ * a snapshot, for instance) must leave a consistent state. Out-of-range
+ * entries are caught (HS_STATUS_BAD_STATE); a slot table holding one token in
+ * two slots is not: a step that selects that token reports either slot.
  */
 typedef struct hs_device_views {
   void* hot;            uint64_t hot_bytes;       /* [R][B][row_bytes] hot buffer rows */
