@@ -108,6 +108,12 @@ void fill_sizes(const hs_config* cfg, int32_t H, const hs::Layout& L, hs_sizes* 
   s->plan_bytes = R * 3 * k * 4;
   s->trial_bytes = R * (uint64_t)hs::trial_words((int)k, (int)B) * 4;
   s->lds_bytes = L.total;
+  // what launches take on a device that allows the full 159 KiB (the direct layout where it fits)
+  const int kk = cfg->top_k, BB = cfg->device_buffer_size;
+  s->lds_bytes_launch = hs::make_direct_layout(kk, BB, (int)H, false, hs::kLdsCap).total;
+  s->lds_bytes_launch_gather = hs::make_direct_layout(kk, BB, (int)H, true, hs::kLdsCap).total;
+  s->token_slot_table = (hs::make_direct_layout(kk, BB, (int)H, false, hs::kLdsCap).direct ? 1u : 0u) |
+                        (hs::make_direct_layout(kk, BB, (int)H, true, hs::kLdsCap).direct ? 2u : 0u);
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }

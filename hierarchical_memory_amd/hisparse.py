@@ -47,7 +47,9 @@ class HsSizes(ctypes.Structure):
                 ("tail_bytes", ctypes.c_uint64), ("slot_tok_bytes", ctypes.c_uint64), ("stamp_bytes", ctypes.c_uint64),
                 ("lru_order_bytes", ctypes.c_uint64), ("page_bytes", ctypes.c_uint64), ("step_bytes", ctypes.c_uint64),
                 ("topk_bytes", ctypes.c_uint64), ("out_bytes", ctypes.c_uint64), ("gather_bytes", ctypes.c_uint64),
-                ("plan_bytes", ctypes.c_uint64), ("trial_bytes", ctypes.c_uint64), ("lds_bytes", ctypes.c_uint32)]
+                ("plan_bytes", ctypes.c_uint64), ("trial_bytes", ctypes.c_uint64), ("lds_bytes", ctypes.c_uint32),
+                ("lds_bytes_launch", ctypes.c_uint32), ("lds_bytes_launch_gather", ctypes.c_uint32),
+                ("token_slot_table", ctypes.c_uint32)]
 
 
 def library_path() -> str:

@@ -77,7 +77,8 @@ extern "C" {
  * uint16 token -> slot entry for each of the H host rows fits beside the
  * rest (about 13k + 7B + 14 * ceil(H / 32) + 2H bytes, 4k more for a launch
  * with a gather output), a launch uses that larger layout, up to 159 KiB,
- * and skips ranking the selected ids.
+ * and skips ranking the selected ids (hs_sizes.lds_bytes_launch,
+ * .lds_bytes_launch_gather and .token_slot_table report which launches do).
  */
 typedef struct hs_config {
   int32_t num_requests;       /* R, 1 .. 65535 */
@@ -129,6 +130,11 @@ typedef struct hs_sizes {
   uint64_t plan_bytes;       /* [R][3][k] int32 plan of hs_plan (miss list and row sources) */
   uint64_t trial_bytes;      /* trial records of hs_trial / hs_commit */
   uint32_t lds_bytes;        /* LDS one resolve workgroup needs at least */
+  uint32_t lds_bytes_launch;        /* LDS a resolve / plan launch without a gather output takes (device
+                                       allowing 159 KiB): the token -> slot layout where it fits */
+  uint32_t lds_bytes_launch_gather; /* the same for a launch with a gather output (fused gather, trial) */
+  uint32_t token_slot_table;        /* bit 0: launches without a gather output use the token -> slot table;
+                                       bit 1: launches with one do */
 } hs_sizes;
 
 typedef struct hs_ctx hs_ctx;

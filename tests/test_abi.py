@@ -135,3 +135,22 @@ def test_build_script_loads_without_the_built_library():
             "assert 'hierarchical_memory_amd' not in sys.modules, 'the package was imported'")
     res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+
+
+def test_token_slot_table_where_it_fits():
+    """Launches take a uint16 token -> slot entry per host row where it fits beside the rest in 159 KiB (about
+    13k + 7B + 14 ceil(H/32) + 2H bytes, 4k more with a gather output); elsewhere they keep the rank layout."""
+    cap = 159 * 1024
+    # (k, B, H, expected bits): 256-request shape without a gather output only, 32-request and single-request
+    # shapes both, hybrid and sweep shapes neither
+    cases = ((2048, 4096, 40960, 1), (2048, 4096, 33024, 3), (256, 512, 4096, 3), (2048, 4096, 131072, 0),
+             (2048, 2048, 65536, 0), (2048, 6144, 65536, 0))
+    for k, B, H, bits in cases:
+        s = hm.hs_required_sizes(hm.config(2, k, B, 0.0, 1152, H))
+        assert s.token_slot_table == bits, (k, B, H, s.token_slot_table)
+        for bit, got, extra in ((1, s.lds_bytes_launch, 0), (2, s.lds_bytes_launch_gather, 4 * k)):
+            if bits & bit:
+                est = 13 * k + 7 * B + 14 * ((H + 31) // 32) + 2 * H + extra
+                assert est <= got <= est + 512 and got <= cap, (k, B, H, bit, got, est)
+            else:
+                assert got == s.lds_bytes, (k, B, H, bit, got, s.lds_bytes)
