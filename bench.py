@@ -676,7 +676,7 @@ def main() -> int:
     log(f"[bench] {K} steps in {elapsed_ms:.1f} ms ({launch_ms:.3f} ms/step, wall {wall:.2f} s): "
         f"{value / 1e6:.1f} M entries/s, misses/request-step {total_miss / (K * R):.1f}, miss copy {miss_gbps:.1f} GB/s")
     rep = {
-        "metric": "resolved top-k entries/s (+ miss-copy GB/s vs host link, HBM), 1 GPU",
+        "metric": "resolved top-k entries/s + miss-copy GB/s vs host-link & HBM peak, 1 GPU",
         "value": value,
         "unit": "entries/s",
         "n_gpus": 1,
