@@ -381,14 +381,18 @@ def test_shared_missed_token_array_near_the_lds_limit():
     p.close()
 
 
-def test_token_slot_table_beside_the_rank_path():
+@pytest.mark.parametrize("base,bits", [(workload.CONC_256, 1), (workload.GROW_32, 3)], ids=["256req_shape", "32req_shape"])
+def test_token_slot_table_beside_the_rank_path(base, bits):
     """At the 256-request shape (k = 2048, B = 4096, H = 40960) a launch without a gather output has LDS for a
     token -> slot entry per host row, so hit slots write their index under their token and the selected ids are
     not ranked; a request whose selection repeats an id ranks them instead, in the same launch. With a gather
-    output the table does not fit and every request ranks. Requests 1 and 3 repeat an id on odd steps; fused
-    without and with a gather, and plan + copy, step by step against the oracle."""
+    output the table does not fit there and every request ranks; at the 32-request shape (H = 33024) it fits with
+    one too. Requests 1 and 3 repeat an id on odd steps; fused without and with a gather, and plan + copy, step
+    by step against the oracle."""
     import hierarchical_memory_amd as hm
-    w = workload.CONC_256.with_(name="conc_shape_4req", num_requests=4, steps=8)
+    w = base.with_(name=base.name + "_4req", num_requests=4, steps=8)
+    sizes = hm.hs_required_sizes(hm.config(w.num_requests, w.top_k, w.buffer_slots, 0.0, w.row_bytes, w.host_rows))
+    assert sizes.token_slot_table == bits
     ids = workload.streams(w)
     ids[1, 1::2, 7] = ids[1, 1::2, 3]
     ids[3, 1::2, 100] = ids[3, 1::2, 2000]
