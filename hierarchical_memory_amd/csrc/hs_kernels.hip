@@ -840,41 +840,52 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   }
   const size_t rB = (size_t)r * B, rH = (size_t)r * H, rk = (size_t)r * k;
   const uint16_t* nord = reinterpret_cast<const uint16_t*>(rec + kTrialHead + 4 * k);
-  for (int s = tid; s < B; s += blockDim.x) used[s] = 0;
-  __syncthreads();
-  // four strided entries per thread at a time, all loaded before any is stored: the record and the order
-  // list are both global memory, so a store could otherwise hold back the next entry's load
-  const int nt = blockDim.x;
-  for (int p0 = tid; p0 < B; p0 += 4 * nt) {
-    int o[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) o[u] = p0 + u * nt < B ? nord[p0 + u * nt] : B;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = p0 + u * nt;
-      if (p >= B || o[u] >= B) continue;  // past the end, or a corrupt record
-      a.order[rB + p] = (uint16_t)o[u];
-      if (p >= u0) used[o[u]] = 1;
-    }
-  }
-  __syncthreads();
-  for (int s = tid; s < B; s += blockDim.x)
-    if (used[s]) a.stamp[rB + s] = t;
   const int32_t* tok = rec + kTrialHead;
   const int32_t* slot = tok + k;
   const int32_t* evicted = slot + k;
   const int32_t* pos = evicted + k;
-  for (int j = tid; j < m; j += blockDim.x) {
-    const int x = tok[j], v = slot[j], y = evicted[j], i = pos[j];
+  const int nt = blockDim.x;
+  // The first round of every record load (four order entries and one miss per thread) is issued before the
+  // flags are cleared, so the two lists cost one round trip; later rounds, for larger shapes, load as they go.
+  int o0[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) o0[u] = tid + u * nt < B ? nord[tid + u * nt] : B;
+  int x0 = -1, v0 = -1, y0 = -1, i0 = -1;
+  if (tid < m) { x0 = tok[tid]; v0 = slot[tid]; y0 = evicted[tid]; i0 = pos[tid]; }
+  for (int s = tid; s < B; s += nt) used[s] = 0;
+  __syncthreads();
+  // the new order and its tail's flags
+  auto place = [&](int p, int o) {
+    if (p >= B || o >= B) return;  // past the end, or a corrupt record
+    a.order[rB + p] = (uint16_t)o;
+    if (p >= u0) used[o] = 1;
+  };
+#pragma unroll
+  for (int u = 0; u < 4; ++u) place(tid + u * nt, o0[u]);
+  // four strided entries per thread at a time, all loaded before any is stored: the record and the order
+  // list are both global memory, so a store could otherwise hold back the next entry's load
+  for (int p0 = tid + 4 * nt; p0 < B; p0 += 4 * nt) {
+    int o[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = p0 + u * nt < B ? nord[p0 + u * nt] : B;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) place(p0 + u * nt, o[u]);
+  }
+  // the victims' table entries, and their slots and gather positions staged for the row copy
+  auto miss_entry = [&](int j, int x, int v, int y, int i) {
     const bool ok = x >= 0 && x < H && v >= 0 && v < B;
     lslot[j] = ok && i >= 0 && i < k ? v : -1;  // a row only for a sound entry
     lpos[j] = i;
-    if (!ok) continue;
+    if (!ok) return;
     if (y >= 0 && y < H) a.page[rH + y] = -1;
     a.page[rH + x] = v;
     a.slot_tok[rB + v] = x;
-  }
+  };
+  if (tid < m) miss_entry(tid, x0, v0, y0, i0);
+  for (int j = tid + nt; j < m; j += nt) miss_entry(j, tok[j], slot[j], evicted[j], pos[j]);
   __syncthreads();
+  for (int s = tid; s < B; s += nt)
+    if (used[s]) a.stamp[rB + s] = t;
   // missed rows, gather output -> victim slots: the slot and position of a chunk come from LDS, so each
   // thread keeps kUnroll 16-byte loads in flight with nothing between them
   const int row16 = a.row16, total = m * row16;
