@@ -190,6 +190,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   const int k = a.k, B = a.B, H = a.H, T = a.T;
   const int W = (int)L.words;
   const bool has_tail = a.tail0 != nullptr;
+  // without a device tail every selected id is a candidate: the candidate set is the selected set
+  if (!has_tail) cbits = sel;
   constexpr bool fifo = kFifo;
   const int32_t t0 = has_tail ? a.tail0[r] : 0;
   const int32_t t = a.step[r];
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     const int wi = s ? (x >> 5) : 0;
     const uint32_t bit = s ? 1u << (x & 31) : 0u;
     const uint32_t old = atomicOr(&sel[wi], bit);
-    atomicOr(&cbits[wi], c == C_CAND ? bit : 0u);
+    if (has_tail) atomicOr(&cbits[wi], c == C_CAND ? bit : 0u);
     repeat |= (old & bit) != 0u;
   };
   auto ids4 = [&](int i, int4 x) {
@@ -282,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) old[u] = atomicOr(&sel[wi[u]], bit[u]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) atomicOr(&cbits[wi[u]], c[u] == C_CAND ? bit[u] : 0u);
+    for (int u = 0; has_tail && u < 4; ++u) atomicOr(&cbits[wi[u]], c[u] == C_CAND ? bit[u] : 0u);
     uint32_t rep = 0u;
 #pragma unroll
     for (int u = 0; u < 4; ++u) rep |= old[u] & bit[u];
