@@ -116,10 +116,10 @@ def copy_probes(hm, torch, np, sw, w, reps: int = 7):
     R, k, B, H, rb = w.num_requests, w.top_k, w.buffer_slots, w.host_rows, w.row_bytes
     m = min(k, H)
     rng = np.random.default_rng(7)
-    seq = np.full((R, 3, k), -1, np.int32)  # the plan layout of hs_plan: tokens, slots, row sources
+    seq = np.full((R, 4, k), -1, np.int32)  # the plan layout of hs_plan: tokens, slots, evicted tokens, sources
     seq[:, 0, :m] = np.arange(m, dtype=np.int32)
     seq[:, 1, :m] = np.arange(m, dtype=np.int32)
-    rnd = np.full((R, 3, k), -1, np.int32)
+    rnd = np.full((R, 4, k), -1, np.int32)
     for r in range(R):
         rnd[r, 0, :m] = rng.choice(H, size=m, replace=False)
         rnd[r, 1, :m] = rng.choice(B, size=m, replace=False)
@@ -308,7 +308,7 @@ def overlap_leg(hm, torch, np, sw, topk, tail0, W, K, w):
         b = t % 2
         if copied[b] is not None:
             main.wait_event(copied[b])  # the copy that read this plan buffer is done
-        hm.hs_plan(sw.ctx, topk[t], tail0, outs[b], miss[t], status[t], plans[b], main)
+        hm.hs_plan(sw.ctx, topk[t], tail0, outs[b], miss[t], status[t], plans[b], main, row_sources=g is not None)
         planned = torch.cuda.Event()
         planned.record(main)
         side.wait_event(planned)

@@ -16,6 +16,8 @@ struct hs_ctx {
   hs::Layout layout;          // the rank layout: what a context of this shape needs at least
   hs::Layout layout_plain;    // launches without a gather output: the direct layout where it fits
   hs::Layout layout_gather;   // launches with one (fused gather, trial)
+  hs::Layout layout_plain_direct, layout_gather_direct;  // the same before the bound tables' alignment is known
+  uint32_t lds_cap;           // LDS a resolve workgroup may take on this device
   int device;
   void* pool_host;       // pinned, mapped host pool
   void* pool_dev;        // its device address
@@ -78,13 +80,18 @@ int check_config(const hs_config* cfg, int32_t* H_out, hs::Layout* L_out) {
       __builtin_mul_overflow(pool, (uint64_t)cfg->row_bytes, &pool) || pool > (1ull << 56))
     return fail(HS_E_INVALID, "the host pool (%d requests x %lld rows x %d bytes) exceeds 2^56 bytes",
                 cfg->num_requests, (long long)H, cfg->row_bytes);
-  const hs::Layout L = hs::make_layout(cfg->top_k, cfg->device_buffer_size, (int)H);
-  // 1 KiB of the 160 KiB of a gfx950 compute unit stays for the kernel's static LDS
-  if (L.total > hs::kLdsCap)
+  // one workgroup's LDS: each kind of launch (with and without a gather output) takes the direct layout where
+  // it fits and the rank layout otherwise; 1 KiB of the 160 KiB of a gfx950 compute unit stays for the kernels'
+  // static LDS
+  const int k = cfg->top_k, B = cfg->device_buffer_size, T = cfg->tail_tokens;
+  const hs::Layout L = hs::make_layout(k, B, (int)H);
+  const uint32_t need = std::max(hs::launch_layout(k, B, (int)H, T, false, hs::kLdsCap).total,
+                                 hs::launch_layout(k, B, (int)H, T, true, hs::kLdsCap).total);
+  if (need > hs::kLdsCap)
     return fail(HS_E_INVALID,
                 "this shape needs %u bytes of LDS per workgroup (top_k %d, buffer %d, host rows %lld), "
                 "more than the 159 KiB one resolve workgroup may use on gfx950",
-                L.total, cfg->top_k, cfg->device_buffer_size, (long long)H);
+                need, k, B, (long long)H);
   *H_out = (int32_t)H;
   *L_out = L;
   return HS_OK;
@@ -105,15 +112,17 @@ void fill_sizes(const hs_config* cfg, int32_t H, const hs::Layout& L, hs_sizes* 
   s->topk_bytes = R * k * 4;
   s->out_bytes = R * k * 4;
   s->gather_bytes = R * k * rb;
-  s->plan_bytes = R * 3 * k * 4;
+  s->plan_bytes = R * 4 * k * 4;
   s->trial_bytes = R * (uint64_t)hs::trial_words((int)k, (int)B) * 4;
-  s->lds_bytes = L.total;
   // what launches take on a device that allows the full 159 KiB (the direct layout where it fits)
-  const int kk = cfg->top_k, BB = cfg->device_buffer_size;
-  s->lds_bytes_launch = hs::make_direct_layout(kk, BB, (int)H, false, hs::kLdsCap).total;
-  s->lds_bytes_launch_gather = hs::make_direct_layout(kk, BB, (int)H, true, hs::kLdsCap).total;
-  s->token_slot_table = (hs::make_direct_layout(kk, BB, (int)H, false, hs::kLdsCap).direct ? 1u : 0u) |
-                        (hs::make_direct_layout(kk, BB, (int)H, true, hs::kLdsCap).direct ? 2u : 0u);
+  const int kk = cfg->top_k, BB = cfg->device_buffer_size, TT = cfg->tail_tokens;
+  const hs::Layout lp = hs::launch_layout(kk, BB, (int)H, TT, false, hs::kLdsCap);
+  const hs::Layout lg = hs::launch_layout(kk, BB, (int)H, TT, true, hs::kLdsCap);
+  s->lds_bytes_rank = L.total;
+  s->lds_bytes_launch = lp.total;
+  s->lds_bytes_launch_gather = lg.total;
+  s->lds_bytes = std::max(lp.total, lg.total);
+  s->token_slot_table = (lp.direct ? 1u : 0u) | (lg.direct ? 2u : 0u);
 }
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -171,12 +180,15 @@ int hs_create(const hs_config* cfg, hs_ctx** out) {
   int lds_max = 0;
   e = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
   if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute(max shared memory per block)");
-  if ((int64_t)L.total + 1024 > (int64_t)lds_max)
-    return fail(HS_E_INVALID, "this shape needs %u bytes of LDS per workgroup, the device allows %d", L.total,
-                lds_max);
+  // the device's own limit: a direct layout that does not fit under it falls back to the rank layout
+  const uint32_t cap = std::min<uint32_t>(hs::kLdsCap, lds_max > 1024 ? (uint32_t)lds_max - 1024u : 0u);
+  const hs::Layout lp = hs::launch_layout(cfg->top_k, cfg->device_buffer_size, (int)H, cfg->tail_tokens, false, cap);
+  const hs::Layout lg = hs::launch_layout(cfg->top_k, cfg->device_buffer_size, (int)H, cfg->tail_tokens, true, cap);
+  if (std::max(lp.total, lg.total) > cap)
+    return fail(HS_E_INVALID, "this shape needs %u bytes of LDS per workgroup, the device allows %d",
+                std::max(lp.total, lg.total), lds_max);
   // The cap on dynamic LDS is an attribute of the kernels, shared by every context on the device: set it to
   // the most any context may use, so a later context of a smaller shape cannot lower it under this one.
-  const uint32_t cap = std::min<uint32_t>(hs::kLdsCap, (uint32_t)lds_max - 1024u);
   e = hs::set_lds_limits(cap, cap);
   if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(resolve kernel LDS)");
 
@@ -185,8 +197,11 @@ int hs_create(const hs_config* cfg, hs_ctx** out) {
   ctx->cfg = *cfg;
   ctx->H = H;
   ctx->layout = L;
-  ctx->layout_plain = hs::make_direct_layout(cfg->top_k, cfg->device_buffer_size, (int)H, false, cap);
-  ctx->layout_gather = hs::make_direct_layout(cfg->top_k, cfg->device_buffer_size, (int)H, true, cap);
+  ctx->layout_plain = lp;
+  ctx->layout_gather = lg;
+  ctx->layout_plain_direct = lp;
+  ctx->layout_gather_direct = lg;
+  ctx->lds_cap = cap;
   ctx->device = dev;
   ctx->pool_bytes = (uint64_t)cfg->num_requests * (uint64_t)H * (uint64_t)cfg->row_bytes;
   // Pinned host memory mapped into the GPU's address space; the resolve kernel reads missed rows
@@ -251,6 +266,19 @@ int hs_bind_device(hs_ctx* ctx, const hs_device_views* v) {
     const int rc = check_device_buffer(ctx, v->tail, "tail");
     if (rc) return rc;
   }
+  // The direct kernel reads and writes each request's slot table and stamps in 16-byte pieces and its order
+  // list in 8-byte ones: with tables less aligned than that, launches take the rank layout.
+  const bool tables16 = aligned(v->slot_tok, 16) && aligned(v->stamp, 16) && aligned(v->lru_order, 8);
+  hs::Layout lp = ctx->layout_plain_direct, lg = ctx->layout_gather_direct;
+  if (!tables16) {
+    if (lp.direct) lp = ctx->layout;
+    if (lg.direct) lg = ctx->layout;
+    if (std::max(lp.total, lg.total) > ctx->lds_cap)
+      return fail(HS_E_INVALID, "this shape needs 16-byte aligned slot_tok and stamp and an 8-byte aligned "
+                                "lru_order (its rank layout does not fit in LDS)");
+  }
+  ctx->layout_plain = lp;
+  ctx->layout_gather = lg;
   ctx->views = *v;
   ctx->bound = true;
   return ok();
@@ -287,7 +315,8 @@ int hs_reset(hs_ctx* ctx, const int32_t* d_request_ids, int32_t n, void* stream)
 namespace {
 
 int resolve_common(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
-                   int32_t* d_status, void* d_gather, int32_t* d_plan, int32_t* d_trial, void* stream) {
+                   int32_t* d_status, void* d_gather, int32_t* d_plan, int32_t plan_flags, int32_t* d_trial,
+                   void* stream) {
   int rc = check_ready(ctx);
   if (rc) return rc;
   if (!d_topk || !d_out || !d_miss || !d_status)
@@ -327,6 +356,7 @@ int resolve_common(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, i
   a.status = d_status;
   a.gather = (hs::v4u*)d_gather;
   a.plan = d_plan;
+  a.plan_sources = (plan_flags & HS_PLAN_ROW_SOURCES) ? 1 : 0;
   a.trial = d_trial;
   a.trial_words = hs::trial_words(a.k, a.B);
   if (d_trial && !aligned(d_trial, 16)) return fail(HS_E_INVALID, "trial buffer is not 16-byte aligned");
@@ -341,19 +371,20 @@ extern "C" {
 
 int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
                int32_t* d_status, void* d_gather, void* stream) {
-  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, d_gather, nullptr, nullptr, stream);
+  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, d_gather, nullptr, 0, nullptr, stream);
 }
 
 int hs_plan(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
-            int32_t* d_status, int32_t* d_plan, void* stream) {
+            int32_t* d_status, int32_t* d_plan, int32_t flags, void* stream) {
   if (!d_plan) return fail(HS_E_INVALID, "plan buffer must not be NULL");
-  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, nullptr, d_plan, nullptr, stream);
+  if (flags & ~HS_PLAN_ROW_SOURCES) return fail(HS_E_INVALID, "unknown plan flags 0x%x", (unsigned)flags);
+  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, nullptr, d_plan, flags, nullptr, stream);
 }
 
 int hs_trial(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
              int32_t* d_status, void* d_gather, int32_t* d_trial, void* stream) {
   if (!d_trial || !d_gather) return fail(HS_E_INVALID, "trial and gather buffers must not be NULL");
-  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, d_gather, nullptr, d_trial, stream);
+  return resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, d_gather, nullptr, 0, d_trial, stream);
 }
 
 int hs_commit(hs_ctx* ctx, const int32_t* d_trial, const void* d_gather, const int32_t* d_accept, int32_t* d_status,
@@ -404,6 +435,7 @@ int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* d_g
   a.hot = (hs::v4u*)ctx->views.hot;
   a.tail = (const hs::v4u*)ctx->views.tail;
   a.gather = (hs::v4u*)d_gather;
+  a.page = ctx->views.page;
   hipError_t e = hs::launch_copy(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "copy launch");
   return ok();

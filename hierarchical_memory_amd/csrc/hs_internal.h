@@ -14,22 +14,38 @@ constexpr int kMaxSlots = 65535;          // slot ids fit the uint16 LRU order l
 
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte chunk of a row
 
-// LDS carve-up of one resolve workgroup (byte offsets; every section 16-byte aligned). The token sets are
-// kept as separate arrays of 32-bit words (consecutive words in consecutive LDS banks, which spreads the
-// random lookups). Sections reused once dead: the rank -> first position table holds the victim list from
-// phase 4 on, the per-position ranks hold the missed ids from phase 5 on, and the prefix counts of the
-// selected set become the prefix counts of the misses.
+// LDS carve-up of one resolve workgroup (byte offsets; every section 16-byte aligned). Two layouts:
+//
+// Rank layout (resolve_kernel, every accepted shape): the selected ids and the ids found in a slot are kept
+// as bitmaps over token ids, separate arrays of 32-bit words (consecutive words in consecutive LDS banks,
+// which spreads the random lookups); a selected id's rank among the selected ids is a prefix count plus a
+// popcount. Candidates (selected, not resident in the device tail) are the selected bits outside the tail
+// window, which is one contiguous id range, so they need no bitmap of their own. Sections reused once dead:
+// the rank -> first position table holds the victim list from phase 4 on, the per-position ranks hold the
+// missed ids from phase 5 on, and the prefix counts of the selected set become those of the misses.
+//
+// Direct layout (resolve_direct_kernel, where it fits): a uint16 token -> slot table with one entry per host
+// row, never cleared. Each slot writes its index under its token; an id x then hits slot s = t2s[x] exactly
+// when s < B and the slot table holds x at s, so garbage left in the table by earlier work is harmless. Only
+// the missed ids need a bitmap (for their ascending-id ranks). A selection that repeats an id is ranked as in
+// the rank layout, with its arrays placed inside the table's region, dead by then.
 struct Layout {
-  uint32_t ids, cls, rank_slot, rank, stok, ord, sflag, sel, cbits, hbits, selpre, first, mpre, vict, mtok, gsrc,
-      misc;
-  uint32_t bm_end;  // end of the three bitmaps (sel, cbits, hbits are adjacent and cleared together)
-  uint32_t t2s;     // token -> slot table (uint16 per host row) of the direct layout
-  uint32_t direct;  // 1: direct layout (t2s valid; rank_slot, rank, first and selpre live inside it)
+  // rank layout
+  uint32_t ids, cls, rank_slot, rank, ord, hbits;
+  // both
+  uint32_t stok, sflag, sel, selpre, first, mpre, vict, mtok, gsrc, misc;
+  // direct layout
+  uint32_t mbits, rbits, t2s;
+  uint32_t bm_end;  // rank layout: end of the two bitmaps (sel, hbits are adjacent and cleared together)
+  uint32_t direct;  // 1: direct layout
   uint32_t words;   // bitmap words = ceil(H / 32)
   uint32_t total;
 };
 
 inline uint32_t align16(uint64_t x) { return (uint32_t)((x + 15) & ~uint64_t(15)); }
+
+// misc words: one slot array of wave totals per block scan, per-wave flag words, then single words
+constexpr int kMiscWords = 8 * kWaves + 8;
 
 inline Layout make_layout(int k, int B, int H) {
   Layout L{};
@@ -44,7 +60,6 @@ inline Layout make_layout(int k, int B, int H) {
   L.ord = take(2ull * B);
   L.sflag = take(1ull * B);
   L.sel = take(4ull * L.words);     // selected ids (candidates and resident)
-  L.cbits = take(4ull * L.words);   // candidate ids (not resident)
   L.hbits = take(4ull * L.words);   // candidate ids found in a slot
   L.bm_end = (uint32_t)off;
   L.selpre = take(2ull * L.words);  // uint16 prefix counts (k <= 8192)
@@ -52,7 +67,7 @@ inline Layout make_layout(int k, int B, int H) {
   L.mpre = L.selpre;
   L.vict = L.first;
   L.gsrc = take(4ull * k);
-  L.misc = take(4ull * (4 * kWaves + 8));
+  L.misc = take(4ull * kMiscWords);
   // The missed tokens get an array of their own when it still fits: then a selection without repeated ids
   // reads each hit slot from rank_slot while pairing, with no pass of its own. Otherwise they reuse rank_slot,
   // dead once every position has taken its slot in that pass.
@@ -62,45 +77,46 @@ inline Layout make_layout(int k, int B, int H) {
   return L;
 }
 
-// The direct layout, where it fits in cap bytes (else the layout above): every host row of the request has a
-// uint16 entry in a token -> slot table, so a slot holding a selected token writes its index under the token
-// itself and the selected ids need no ranks. Nothing reads an entry whose token has no hit bit, so the table
-// is never cleared. A launch whose selection repeats an id still ranks (the lowest position holding an id
-// keeps it): the rank arrays and the selected set's prefix counts then live inside the table's region, which
-// that launch does not use otherwise. The miss prefixes, the victim list and the missed tokens get arrays of
-// their own; the per-position row sources only when the launch gathers rows.
-inline Layout make_direct_layout(int k, int B, int H, bool gather, uint64_t cap) {
+// Ids and slots per thread of the direct kernel: (2, 4) for k <= 2048 and B <= 4096, else (8, 8); it holds at
+// most three bitmap words per thread and clears its two bitmaps with at most two 16-byte stores per thread.
+constexpr int kDirectMaxSlots = 8 * kThreads;
+
+// The direct layout for k, B, H (tail of T rows), or one with direct == 0 where the direct kernel cannot take
+// the shape: it does not fit in cap bytes, B is not a multiple of 4 or passes the kernel's limit, or the
+// bitmaps pass the per-thread limits above. The per-position row sources only for launches that gather rows.
+// The token -> slot table has a spare entry at index H, where slots without a valid token write.
+inline Layout make_direct_layout(int k, int B, int H, int T, bool gather, uint64_t cap) {
   Layout L{};
   L.words = (uint32_t)(((uint64_t)H + 31) / 32);
   uint64_t off = 0;
   auto take = [&](uint64_t bytes) { uint32_t o = (uint32_t)off; off = align16(off + bytes); return o; };
-  L.ids = take(4ull * k);
-  L.cls = take(1ull * k);
   L.stok = take(4ull * B);
-  L.ord = take(2ull * B);
-  L.sflag = take(1ull * B);
-  L.sel = take(4ull * L.words);
-  L.cbits = take(4ull * L.words);
-  L.hbits = take(4ull * L.words);
-  L.bm_end = (uint32_t)off;
+  L.sflag = take(4ull * (((uint64_t)B + 3) / 4));   // one byte per slot, read and or-ed as 32-bit words
+  L.mbits = take(4ull * L.words);
+  L.rbits = take(4ull * (((uint64_t)T + 31) / 32));
   L.mpre = take(2ull * L.words);
   L.vict = take(4ull * k);
   L.mtok = take(4ull * k);
-  L.gsrc = gather ? take(4ull * k) : 0u;  // unused without a gather (a plan launch writes the sources out)
-  L.misc = take(4ull * (4 * kWaves + 8));
-  // the table's region, with the rank path's arrays inside it
+  L.gsrc = gather ? take(4ull * k) : 0u;
+  L.misc = take(4ull * kMiscWords);
+  // the table's region, holding the repeat path's arrays once the table is dead
   const uint64_t region = off;
   L.t2s = (uint32_t)region;
-  L.rank_slot = take(4ull * k);
-  L.rank = take(4ull * k);
-  L.first = take(4ull * k);
+  L.sel = take(4ull * L.words);
   L.selpre = take(2ull * L.words);
-  const uint64_t table = align16(2ull * (uint64_t)H);
+  L.first = take(4ull * k);
+  const uint64_t table = align16(2ull * (uint64_t)H + 2);
   if (off < region + table) off = region + table;
   L.total = (uint32_t)off;
-  L.direct = 1u;
-  if (off > cap) return make_layout(k, B, H);
+  const bool bitmaps_ok = L.words <= 3u * kThreads && (L.mpre - L.mbits) <= 2u * 16u * kThreads;
+  L.direct = (off <= cap && B <= kDirectMaxSlots && B % 4 == 0 && bitmaps_ok) ? 1u : 0u;
   return L;
+}
+
+// The layout a launch takes: the direct one where it fits, else the rank one.
+inline Layout launch_layout(int k, int B, int H, int T, bool gather, uint64_t cap) {
+  const Layout D = make_direct_layout(k, B, H, T, gather, cap);
+  return D.direct ? D : make_layout(k, B, H);
 }
 
 struct ResolveArgs {
@@ -122,8 +138,10 @@ struct ResolveArgs {
   int32_t* miss;
   int32_t* status;
   v4u* gather;
-  int32_t* plan;    // non-null: plan-only launch, [R][3][k] (missed tokens, their victim slots, the source of
-                    // each position's row: slot, B + tail row, -1 none, -2 - j the j-th miss)
+  int32_t* plan;    // non-null: plan-only launch, [R][4][k] (missed tokens, their victim slots, the tokens
+                    // the victims held (-1: empty), and with plan_sources the source of each position's row: slot,
+                    // B + tail row, -1 none, -2 - j the j-th miss)
+  int32_t plan_sources;
   int32_t* trial;   // non-null: trial launch, [R][trial_words]
   int64_t trial_words;
 };
@@ -150,10 +168,11 @@ struct CommitArgs {
 struct CopyArgs {
   int32_t R, k, B, H, T, row16;
   int32_t rows;         // with a gather: selected rows per workgroup
-  const int32_t* plan;  // [R][3][k]
+  const int32_t* plan;  // [R][4][k]
   const int32_t* miss;  // [R]
   const v4u* host;
   v4u* hot;
+  int32_t* page;        // [R][H]: the plan's page-table updates are applied here
   const v4u* tail;      // [R][T][row16] or nullptr
   v4u* gather;          // [R][k][row16] or nullptr (no gather)
 };

@@ -1,53 +1,47 @@
 // HIP kernels of the HiSparse swap-in path for gfx950 (MI355X).
 //
-// resolve_kernel: one 1024-thread workgroup per request performs one decode
-// step of the swap-in kernel the pages describe ("HiSparse: Turbocharging
-// Sparse Attention with Hierarchical Memory", section 2, steps 1-3;
-// 「HiSparse：階層化メモリシステムによるスパースアテンションの加速」, section
-// 「効率的なSwap-inカーネル」), with the device-resident tail and the fused
-// gather of "vLLM GLM 5.3 最適化: Hybrid HiSparse オフローディング", section 2
-// Mixed Residency:
-//   phase 0  coalesced loads of the selected ids, the slot->token table and the
-//            LRU order list into LDS, all issued before any is consumed; ids
-//            classified (padding, bad, resident, candidate) and put straight
-//            into LDS bitmaps over token ids: the selected set, and the
-//            candidates among it (not resident);
-//   phase 1  popcount prefix over the selected bitmap's words, so the rank of a
-//            selected id among the selected ids is one lookup (skipped where the
-//            LDS holds a token -> slot table for every host row of the request,
-//            and the selection repeats no id: a hit slot then writes its index
-//            under its token, and a position reads it there);
-//   phase 2  in one pass, every selected position takes its id's rank and, when
-//            phase 0 saw an id twice, bids for it (the lowest position wins, so a
-//            repeated id is resolved without any order-dependent atomic) while
-//            every slot tests its token
-//            against the bitmap: a hit, found in O(1) and recorded under the
-//            token's rank, also marked in a hit bitmap, so the missed ids are the
-//            candidate bits without a hit bit;
-//   phase 3  one block scan gives each missed id its rank among the misses
-//            (ascending id) and each non-hit slot its rank in the LRU order (the
-//            first m are the victims); the surviving candidates open the new
-//            LRU order;
-//   phase 4  j-th missed id -> j-th victim: page table, slot table, stamps,
-//            outputs; the hit and victim slots close the new LRU order in slot
-//            order;
-//   phase 5  wavefronts copy the missed rows, 16 bytes per lane, straight from
-//            mapped pinned host memory into the HBM slots (and every selected
-//            row into the gather output when fused).
-// Scans run over thread-contiguous chunks: a DPP scan inside each wave, one
-// exchange of the 16 wave totals through LDS, which each wave scans again in
-// one DPP row. No result depends on the order of LDS atomics (they are OR and
-// MIN only).
+// One 1024-thread workgroup per request performs one decode step of the swap-in kernel the pages describe
+// ("HiSparse: Turbocharging Sparse Attention with Hierarchical Memory", section 2, steps 1-3;
+// 「HiSparse：階層化メモリシステムによるスパースアテンションの加速」, section 「効率的なSwap-inカーネル」), with the
+// device-resident tail and the fused gather of "vLLM GLM 5.3 最適化: Hybrid HiSparse オフローディング", section 2
+// Mixed Residency. Two kernels do it, by LDS layout.
 //
-// The LRU order list keeps each request's slots sorted by (stamp, slot). After
-// a step, the non-victim candidates keep their stamps and relative order, and
-// every hit or victim slot now carries stamp t, larger than any older stamp, so
-// appending them in slot order keeps the list sorted. Empty slots (stamp -1)
-// start at the front in slot order after a reset.
+// resolve_direct_kernel (where a uint16 token -> slot entry for every host row fits in LDS):
+//   A  coalesced loads of the selected ids, the slot table and the LRU order list, all issued before any is
+//      consumed; each slot writes its index under its token in the (never cleared) token -> slot table;
+//   B  each selected id is tested from its own side: it hits slot s = t2s[x] exactly when s < B and slot s
+//      holds x, so stale table entries cannot fake a hit; a hit marks its slot, a miss its bit in a bitmap
+//      of missed ids (an already-set bit or flag means the selection repeats an id, which is then ranked as
+//      in the rank kernel: the lowest position keeps it);
+//   C  one block scan ranks the misses (ascending id, popcounts of the bitmap) and the non-hit slots in LRU
+//      order; the first m of these are the victims, the others open the new order;
+//   D  j-th missed id -> j-th victim: page table, slot table, stamps, outputs; a second scan closes the new
+//      order with the slots used this step, in slot order;
+//   E  the missed rows are copied from mapped pinned host memory (and every selected row gathered when fused).
+// Ids and order entries stay in registers from A to D; there are five barriers.
 //
-// FIFO replacement (the alternative to LRU a request can be configured with)
-// takes victims the same way, but a hit does not refresh its stamp: hits keep
-// their place in the list and only the victims, stamped t, move to its end.
+// resolve_kernel (every shape, the rank layout):
+//   phase 0  the same loads, staged in LDS; ids classified and put into a bitmap of selected ids;
+//   phase 1  popcount prefix over the bitmap's words, so the rank of a selected id is one lookup;
+//   phase 2  every selected position takes its id's rank and, when phase 0 saw an id twice, bids for it (the
+//            lowest position wins, without order-dependent atomics) while every slot tests its token against
+//            the bitmap: a hit, recorded under the token's rank and marked in a hit bitmap;
+//   phase 3  one block scan ranks the misses (selected ids outside the tail window and not hit) and the
+//            non-hit slots in LRU order, as in C above;
+//   phase 4  as D above;
+//   phase 5  as E above.
+// Scans run over thread-contiguous chunks: a DPP scan inside each wave, one exchange of the 16 wave totals
+// through LDS, which each wave scans again in one DPP row. No result depends on the order of LDS atomics
+// (they are OR and MIN only, and which of two equal ids a bit or flag records is never used).
+//
+// The LRU order list keeps each request's slots sorted by (stamp, slot). After a step, the non-victim
+// candidates keep their stamps and relative order, and every hit or victim slot now carries stamp t, larger
+// than any older stamp, so appending them in slot order keeps the list sorted. Empty slots (stamp -1) start at
+// the front in slot order after a reset.
+//
+// FIFO replacement (the alternative to LRU a request can be configured with) takes victims the same way, but
+// a hit does not refresh its stamp: hits keep their place in the list and only the victims, stamped t, move to
+// its end.
 #include "hs_internal.h"
 
 #include <climits>
@@ -61,9 +55,11 @@ enum : int8_t { C_PAD = 0, C_BAD = 1, C_DUP = 2, C_RES = 3, C_CAND = 4 };
 constexpr int kStatusBadId = 1, kStatusDupId = 2, kStatusBadState = 4, kStatusStale = 8;
 constexpr int kUnroll = 4;  // 16-byte loads each thread keeps in flight in the gather loop
 
-// misc words in LDS: one slot array of wave totals per block scan, then the status word
-constexpr int kMiscScanSel = 0, kMiscScanRank = kWaves, kMiscScanTail = 2 * kWaves, kMiscStatus = 3 * kWaves,
-              kMiscRepeat = 3 * kWaves + 1, kMiscBad = 3 * kWaves + 2;
+// misc words in LDS: one slot array of wave totals per block scan, per-wave flag words, then single words
+constexpr int kMiscScanSel = 0, kMiscScanRank = kWaves, kMiscScanTail = 2 * kWaves, kMiscWaveBad = 3 * kWaves,
+              kMiscWaveRep = 4 * kWaves, kMiscWaveSt = 5 * kWaves, kMiscStatus = 8 * kWaves,
+              kMiscRepeat = 8 * kWaves + 1, kMiscBad = 8 * kWaves + 2, kMiscDummy = 8 * kWaves + 4;
+static_assert(kMiscDummy + 4 <= kMiscWords, "misc words (the dummy takes 16 bytes)");
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2, 4, 8 inside each row of 16
 // lanes, then the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).
@@ -96,7 +92,28 @@ __device__ __forceinline__ int block_excl_scan(int v, int* sh, int lane, int wav
   return pre + inc - v;
 }
 
+// True in every lane when any of the 16 per-wave flag words at f is set (they are written before a barrier).
+__device__ __forceinline__ bool any_wave_flag(const int32_t* f, int lane) {
+  return __ballot(lane < kWaves && f[lane < kWaves ? lane : 0] != 0) != 0ull;
+}
+
+// OR of v over the wave (v holds status bits 0..3).
+__device__ __forceinline__ int wave_or_bits(int v) {
+  int o = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) o |= __ballot((v >> b) & 1) != 0ull ? (1 << b) : 0;
+  return o;
+}
+
 __device__ __forceinline__ uint32_t below(int32_t x) { return (1u << (x & 31)) - 1u; }
+
+// Bits of bitmap word w (tokens 32w .. 32w + 31) that lie in [lo, hi), a window already clipped to [0, H)
+// (so every difference below fits in 32 bits).
+__device__ __forceinline__ uint32_t window_bits(int w, int32_t lo, int32_t hi) {
+  const int a = min(max(lo - 32 * w, 0), 32), b = min(max(hi - 32 * w, 0), 32);
+  const uint32_t below_b = b >= 32 ? ~0u : (1u << b) - 1u, below_a = a >= 32 ? ~0u : (1u << a) - 1u;
+  return below_b & ~below_a;
+}
 
 // Element i of an array whose byte size stays below 4 GiB (per-request rows of k or B entries): the byte
 // offset is formed in 32 bits, so a store takes the scalar-base + 32-bit-offset form.
@@ -148,12 +165,90 @@ __device__ __forceinline__ void trial_header(const ResolveArgs& a, int r, int m,
   rec[3] = 0;
 }
 
+// A request whose state tables hold impossible values: every output -1 (zero rows gathered), no miss, status
+// HS_STATUS_BAD_STATE; nothing of its state is changed.
+template <int kMode>
+__device__ __forceinline__ void refuse_request(const ResolveArgs& a, int r, int tid) {
+  const size_t rk = (size_t)r * a.k;
+  for (int i = tid; i < a.k; i += kThreads) a.out[rk + i] = -1;
+  if (kMode == kPlan && a.plan_sources)
+    for (int i = tid; i < a.k; i += kThreads) a.plan[4 * rk + 3 * (size_t)a.k + i] = -1;
+  if (kMode != kPlan && a.gather) {
+    v4u* gr = a.gather + rk * a.row16;
+    const v4u z = {0u, 0u, 0u, 0u};
+    for (int c = tid; c < a.k * a.row16; c += kThreads) gr[c] = z;
+  }
+  if (tid == 0) { a.miss[r] = 0; a.status[r] = kStatusBadState; }
+  if (kMode == kTrial && tid == 0) trial_header(a, r, 0, 0, -1);
+}
+
+// Phase E / 5: the rows of a fused or trial launch. Without a gather output, the missed rows go from the host
+// pool into their slots; with one, every selected row goes to the output (a miss's straight from the host
+// pool, also into its slot unless this is a trial), as gsrc says: slot, B + tail row, -1 none, -2 - j miss j.
+// mtok, vict and gsrc are LDS arrays made visible by a barrier before the call.
+template <int kMode>
+__device__ __forceinline__ void rows_phase(const ResolveArgs& a, int r, int m, const int32_t* mtok,
+                                           const int32_t* vict, const int32_t* gsrc, int tid) {
+  const int row16 = a.row16, k = a.k, B = a.B;
+  const v4u* hostr = a.host + (size_t)r * a.H * (size_t)row16;
+  v4u* hotr = a.hot + (size_t)r * B * (size_t)row16;
+  if (a.gather == nullptr) {
+    // The host link is saturated with about 128K 16-byte loads in flight over the whole chip; more than that
+    // only queues and costs throughput, so the host sizes (copy_threads, copy_unroll) per request.
+    const int total = m * row16, nt = a.copy_threads;
+    if (tid < nt) {
+      if (a.copy_unroll == 1) copy_missed_rows<1>(hostr, hotr, mtok, vict, total, row16, tid, nt);
+      else if (a.copy_unroll == 2) copy_missed_rows<2>(hostr, hotr, mtok, vict, total, row16, tid, nt);
+      else copy_missed_rows<4>(hostr, hotr, mtok, vict, total, row16, tid, nt);
+    }
+    return;
+  }
+  const int total = k * row16;
+  const v4u* tailr = a.tail + (size_t)r * a.T * row16;
+  v4u* gr = a.gather + (size_t)r * k * (size_t)row16;
+  for (int c0 = tid; c0 < total; c0 += kThreads * kUnroll) {
+    v4u v[kUnroll];
+    long long hot_dst[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = c0 + u * kThreads;
+      hot_dst[u] = -1;
+      v[u] = v4u{0u, 0u, 0u, 0u};
+      if (c < total) {
+        const int i = c / row16, q = c - i * row16;
+        const int g = gsrc[i];
+        if (g <= -2) {
+          const int j = -2 - g;
+          v[u] = load_host(hostr + (size_t)mtok[j] * row16 + q);
+          if (kMode != kTrial) hot_dst[u] = (long long)vict[j] * row16 + q;
+        } else if (g >= B) {
+          v[u] = tailr[(size_t)(g - B) * row16 + q];
+        } else if (g >= 0) {
+          v[u] = hotr[(size_t)g * row16 + q];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = c0 + u * kThreads;
+      if (c < total) {
+        // streamed in a fused step (nothing reads the output back in this launch, and it leaves less to
+        // write back when the launch ends); plain in a trial, whose commit reads the missed rows back
+        if (kMode == kTrial) gr[c] = v[u];
+        else __builtin_nontemporal_store(v[u], gr + c);
+        if (hot_dst[u] >= 0) hotr[hot_dst[u]] = v[u];
+      }
+    }
+  }
+}
+
 }  // namespace
 
 // kMode selects what a launch does with the step it has ranked:
 //   kFused: commit the step and copy the rows (hs_resolve);
-//   kPlan:  commit the step and write the miss list (token, victim slot) to a.plan instead of copying
-//           rows; copy_kernel then moves the rows, possibly on another stream (hs_plan);
+//   kPlan:  commit the step, except the page table, and write the miss list (token, victim slot, evicted
+//           token), and on request each position's row source, to a.plan instead of copying rows; copy_kernel
+//           then moves the rows and updates the page table, possibly on another stream (hs_plan);
 //   kTrial: commit nothing; write a trial record (the new LRU order and, per miss, token, victim slot,
 //           evicted token and position) and gather every selected row, the missed ones straight from the
 //           host pool; commit_kernel applies accepted records later (hs_trial / hs_commit).
@@ -170,7 +265,6 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   uint16_t* ord = (uint16_t*)(smem + L.ord);
   uint8_t* sflag = smem + L.sflag;  // 1: hit this step, 2: victim this step
   uint32_t* sel = (uint32_t*)(smem + L.sel);
-  uint32_t* cbits = (uint32_t*)(smem + L.cbits);
   uint32_t* hbits = (uint32_t*)(smem + L.hbits);
   uint16_t* selpre = (uint16_t*)(smem + L.selpre);
   uint16_t* mpre = (uint16_t*)(smem + L.mpre);
@@ -178,7 +272,6 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   int32_t* vict = (int32_t*)(smem + L.vict);
   int32_t* mtok = (int32_t*)(smem + L.mtok);
   int32_t* gsrc = (int32_t*)(smem + L.gsrc);
-  uint16_t* t2s = (uint16_t*)(smem + L.t2s);         // direct layout: token -> slot that holds it (hit)
   int32_t* misc = (int32_t*)(smem + L.misc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -190,8 +283,6 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   const int k = a.k, B = a.B, H = a.H, T = a.T;
   const int W = (int)L.words;
   const bool has_tail = a.tail0 != nullptr;
-  // without a device tail every selected id is a candidate: the candidate set is the selected set
-  if (!has_tail) cbits = sel;
   constexpr bool fifo = kFifo;
   const int32_t t0 = has_tail ? a.tail0[r] : 0;
   const int32_t t = a.step[r];
@@ -202,18 +293,27 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   int32_t* const page_r = a.page + rH;
   int32_t* const stamp_r = a.stamp + rB;
   int32_t* const slot_tok_r = a.slot_tok + rB;
-  int32_t* const plan_r = a.plan + 3 * rk;  // used by plan launches only
+  int32_t* const plan_r = a.plan + 4 * rk;  // used by plan launches only
+  const bool sources = kMode == kPlan && a.plan_sources != 0;
   // thread-contiguous chunks of bitmap words and of slots / order positions
   const int cw = (W + kThreads - 1) / kThreads, w0 = min(W, tid * cw), w1 = min(W, w0 + cw);
   const int cb = (B + kThreads - 1) / kThreads, s0 = min(B, tid * cb), s1 = min(B, s0 + cb);
   // x - t0 is exact in uint32 once x >= t0, whatever the signs
   auto resident = [&](int32_t x) { return has_tail && x >= t0 && (uint32_t)x - (uint32_t)t0 < (uint32_t)T; };
+  // the tail window clipped to the host rows (uniform), and the candidates of a bitmap word: selected ids
+  // outside it
+  const int32_t win_lo = has_tail ? (int32_t)min<int64_t>(max<int64_t>(t0, 0), H) : 0;
+  const int32_t win_hi = has_tail ? (int32_t)min<int64_t>(max<int64_t>((int64_t)t0 + T, 0), H) : 0;
+  // words that the window touches at all (uniform); elsewhere the mask is zero and is not computed
+  const int win_w0 = win_lo >> 5, win_w1 = win_hi > win_lo ? (win_hi - 1) >> 5 : -1;
+  auto wmask = [&](int w) { return (w >= win_w0 && w <= win_w1) ? window_bits(w, win_lo, win_hi) : 0u; };
+  auto cand_word = [&](int w) { return has_tail ? sel[w] & ~wmask(w) : sel[w]; };
   int st = 0;
 
-  // ---- phase 0: stage and classify, and build the selected and candidate bitmaps. The first round of every
-  // global load of the phase is issued before any of them is consumed (one HBM round trip for the common
-  // shapes), as 16-byte vectors when the sizes allow; LDS scratch is cleared, behind a barrier, while they are
-  // in flight, so each id goes into the bitmaps straight from the register it arrives in.
+  // ---- phase 0: stage and classify, and build the bitmap of selected ids. The first round of every global
+  // load of the phase is issued before any of them is consumed (one HBM round trip for the common shapes), as
+  // 16-byte vectors when the sizes allow; LDS scratch is cleared, behind a barrier, while they are in flight,
+  // so each id goes into the bitmap straight from the register it arrives in.
   int bad = 0, repeat = 0;
   const bool vecB = (B & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.slot_tok + rB) & 15) == 0) &&
                     ((reinterpret_cast<uintptr_t>(a.order + rB) & 7) == 0);
@@ -227,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   if (tid < n4B) { y0 = st4[tid]; o0 = or4[tid]; }
   if (tid < n4k) x0 = tk4[tid];
   {
-    // the three bitmaps are adjacent, each padded to 16 bytes: cleared together in 16-byte stores
+    // the two bitmaps are adjacent, each padded to 16 bytes: cleared together in 16-byte stores
     uint4* bm = reinterpret_cast<uint4*>(smem + L.sel);
     const int n16 = (int)((L.bm_end - L.sel) >> 4);
     for (int q = tid; q < n16; q += kThreads) bm[q] = make_uint4(0u, 0u, 0u, 0u);
@@ -253,15 +353,13 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     st |= badid ? kStatusBadId : 0;
     return x == -1 ? C_PAD : badid ? C_BAD : res ? C_RES : C_CAND;
   };
-  // a selected id (candidate or resident) goes into the selected bitmap, a candidate also into the candidate
-  // bitmap; finding its bit already set means the selection repeats an id. Without branches: an id that is
-  // not selected ORs nothing into word 0.
+  // a selected id (candidate or resident) goes into the bitmap; finding its bit already set means the
+  // selection repeats an id. Without branches: an id that is not selected ORs nothing into word 0.
   auto mark = [&](int32_t x, int8_t c) {
     const bool s = c == C_CAND || c == C_RES;
     const int wi = s ? (x >> 5) : 0;
     const uint32_t bit = s ? 1u << (x & 31) : 0u;
     const uint32_t old = atomicOr(&sel[wi], bit);
-    if (has_tail) atomicOr(&cbits[wi], c == C_CAND ? bit : 0u);
     repeat |= (old & bit) != 0u;
   };
   auto ids4 = [&](int i, int4 x) {
@@ -283,8 +381,6 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     // what mark does, for four ids at once: every atomic is issued before the first result is looked at
 #pragma unroll
     for (int u = 0; u < 4; ++u) old[u] = atomicOr(&sel[wi[u]], bit[u]);
-#pragma unroll
-    for (int u = 0; has_tail && u < 4; ++u) atomicOr(&cbits[wi[u]], c[u] == C_CAND ? bit[u] : 0u);
     uint32_t rep = 0u;
 #pragma unroll
     for (int u = 0; u < 4; ++u) rep |= old[u] & bit[u];
@@ -321,9 +417,6 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   __syncthreads();
   bad = misc[kMiscBad];
   const bool repeats = misc[kMiscRepeat] != 0;  // rare: only then do positions bid for their id's rank
-  // direct: a hit slot writes its index under its token in t2s, and no selected id needs a rank (phase 1 and
-  // the per-position half of phase 2 drop out); a selection that repeats an id ranks as below
-  const bool direct = L.direct != 0u && !repeats;
   if (repeats && !bad) {
     for (int i = tid; i < k; i += kThreads) first[i] = INT_MAX;
     __syncthreads();
@@ -353,19 +446,12 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
 
   if (bad) {
     // impossible state: leave the request untouched
-    for (int i = tid; i < k; i += kThreads) a.out[rk + i] = -1;
-    if (kMode != kPlan && a.gather) {
-      v4u* gr = a.gather + rk * a.row16;
-      const v4u z = {0u, 0u, 0u, 0u};
-      for (int c = tid; c < k * a.row16; c += kThreads) gr[c] = z;
-    }
-    if (tid == 0) { a.miss[r] = 0; a.status[r] = kStatusBadState; }
-    if (kMode == kTrial && tid == 0) trial_header(a, r, 0, 0, -1);
+    refuse_request<kMode>(a, r, tid);
     return;
   }
 
   // ---- phase 1: prefix counts of the selected bitmap (the rank of a selected id is one lookup)
-  if (!direct) {
+  {
     int cnt = 0;
     uint32_t v[4] = {0u, 0u, 0u, 0u};
     if (wvec) {
@@ -389,9 +475,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
 
   // ---- phase 2: ranks and the hit test in one pass. Every selected position records the rank of its id and,
   // if the selection repeats an id, bids for it (the lowest position holding an id wins); every slot whose
-  // token is selected records itself under that token's rank (direct: under the token) and marks the token
-  // hit.
-  for (int i = tid; !direct && i < k; i += kThreads) {
+  // token is selected records itself under that token's rank and marks the token hit.
+  for (int i = tid; i < k; i += kThreads) {
     const int8_t c = cls[i];
     if (c == C_CAND || c == C_RES) {
       const int32_t x = ids[i];
@@ -404,8 +489,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     if (y < 0 || resident(y)) return;  // empty, or resident (a resident id takes no slot)
     const uint32_t word = sel[y >> 5];
     if (word & (1u << (y & 31))) {
-      if (direct) t2s[y] = (uint16_t)s;
-      else rank_slot[(int)selpre[y >> 5] + __popc(word & below(y))] = s;
+      rank_slot[(int)selpre[y >> 5] + __popc(word & below(y))] = s;
       sflag[s] = 1;
       atomicOr(&hbits[y >> 5], 1u << (y & 31));
     }
@@ -448,15 +532,17 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     uint32_t mw[4] = {0u, 0u, 0u, 0u};  // a whole chunk's missed-id words, kept for the prefixes below
     if (wvec) {
       uint32_t hw[4];
-      load_words(cbits, mw);
+      load_words(sel, mw);
       load_words(hbits, hw);
+      const bool touched = has_tail && w0 + cw > win_w0 && w0 <= win_w1;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
+        if (touched) mw[u] &= ~window_bits(w0 + u, win_lo, win_hi);
         mw[u] &= ~hw[u];
         cm += __popc(mw[u]);
       }
     } else {
-      for (int w = w0; w < w1; ++w) cm += __popc(cbits[w] & ~hbits[w]);
+      for (int w = w0; w < w1; ++w) cm += __popc(cand_word(w) & ~hbits[w]);
     }
     // a whole chunk keeps its four slots and their flags in registers for the victim pass below: no flag it
     // reads there is written in between (each slot sits at one position of the order)
@@ -482,14 +568,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     ncand = (int)((uint32_t)tot >> 16);
     if (m > ncand) {
       // more misses than free slots: only possible with a corrupt slot table
-      for (int i = tid; i < k; i += kThreads) a.out[rk + i] = -1;
-      if (kMode != kPlan && a.gather) {
-        v4u* gr = a.gather + rk * a.row16;
-        const v4u z = {0u, 0u, 0u, 0u};
-        for (int c = tid; c < k * a.row16; c += kThreads) gr[c] = z;
-      }
-      if (tid == 0) { a.miss[r] = 0; a.status[r] = kStatusBadState; }
-      if (kMode == kTrial && tid == 0) trial_header(a, r, 0, 0, -1);
+      refuse_request<kMode>(a, r, tid);
       return;
     }
     int run = pre & 0xffff;
@@ -498,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     } else {
       for (int w = w0; w < w1; ++w) {
         mpre[w] = (uint16_t)run;
-        run += __popc(cbits[w] & ~hbits[w]);
+        run += __popc(cand_word(w) & ~hbits[w]);
       }
     }
     // LRU: the new order opens with the candidates that stay; FIFO: with every slot that stays (hits keep
@@ -537,19 +616,11 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     int32_t o = -1, g = -1;
     const bool cand = c == C_CAND;
     const int w = x >> 5;
-    uint32_t hw = 0u;
     int32_t hit = -1;
-    if (cand) {
-      if (direct) {
-        hw = hbits[w];
-        hit = (hw >> (x & 31)) & 1u ? (int32_t)t2s[x] : -1;
-      } else {
-        hit = settle ? rnk[i] : rank_slot[rnk[i]];
-      }
-    }
+    if (cand) hit = settle ? rnk[i] : rank_slot[rnk[i]];
     if (cand && hit < 0) {  // a miss
-      if (!direct) hw = hbits[w];
-      const int j = (int)mpre[w] + __popc(cbits[w] & ~hw & below(x));
+      const uint32_t cwd = cand_word(w);
+      const int j = (int)mpre[w] + __popc(cwd & ~hbits[w] & below(x));
       const int v = vict[j];
       const int32_t y = stok[v];  // each victim belongs to exactly one miss
       if (kMode == kTrial) {
@@ -558,6 +629,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
         rec[kTrialHead + k + j] = v;
         rec[kTrialHead + 2 * k + j] = y;
         rec[kTrialHead + 3 * k + j] = i;
+      } else if (kMode == kPlan) {
+        at(plan_r, 2 * k + j) = y;  // the copy updates the page table
       } else {
         if (y >= 0) page_r[y] = -1;  // H rows may pass 4 GiB of page table: 64-bit offsets here
         page_r[x] = v;
@@ -575,7 +648,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     }
     at(out_r, i) = o;
     if (kMode != kPlan && a.gather != nullptr) gsrc[i] = g;  // read by the gather below
-    if (kMode == kPlan) at(plan_r, 2 * k + i) = g;  // where position i's row comes from (hs_copy's gather)
+    if (sources) at(plan_r, 3 * k + i) = g;  // where position i's row comes from (hs_copy's gather)
   }
   // the slots used this step close the new order in slot order: hits and victims (LRU) or victims only
   // (FIFO); the scan's barrier also publishes the LDS writes above
@@ -632,62 +705,435 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   if (kMode == kTrial && tid == 0) trial_header(a, r, m, tail_start, t);
 
   // ---- phase 5: rows (the block scan above ended with a barrier, so mtok and gsrc are visible)
-  const int row16 = a.row16;
-  const v4u* hostr = a.host + rH * (size_t)row16;
-  v4u* hotr = a.hot + rB * (size_t)row16;
-  if (a.gather == nullptr) {
-    // The host link is saturated with about 128K 16-byte loads in flight over the whole chip; more than that
-    // only queues and costs throughput, so the host sizes (copy_threads, copy_unroll) per request.
-    const int total = m * row16, nt = a.copy_threads;
-    if (tid < nt) {
-      if (a.copy_unroll == 1) copy_missed_rows<1>(hostr, hotr, mtok, vict, total, row16, tid, nt);
-      else if (a.copy_unroll == 2) copy_missed_rows<2>(hostr, hotr, mtok, vict, total, row16, tid, nt);
-      else copy_missed_rows<4>(hostr, hotr, mtok, vict, total, row16, tid, nt);
-    }
-  } else {
-    const int total = k * row16;
-    const v4u* tailr = a.tail + (size_t)r * T * row16;
-    v4u* gr = a.gather + rk * (size_t)row16;
-    for (int c0 = tid; c0 < total; c0 += kThreads * kUnroll) {
-      v4u v[kUnroll];
-      long long hot_dst[kUnroll];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * kThreads;
-        hot_dst[u] = -1;
-        v[u] = v4u{0u, 0u, 0u, 0u};
-        if (c < total) {
-          const int i = c / row16, q = c - i * row16;
-          const int g = gsrc[i];
-          if (g <= -2) {
-            const int j = -2 - g;
-            v[u] = load_host(hostr + (size_t)mtok[j] * row16 + q);
-            if (kMode != kTrial) hot_dst[u] = (long long)vict[j] * row16 + q;
-          } else if (g >= B) {
-            v[u] = tailr[(size_t)(g - B) * row16 + q];
-          } else if (g >= 0) {
-            v[u] = hotr[(size_t)g * row16 + q];
-          }
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int c = c0 + u * kThreads;
-        if (c < total) {
-          // streamed in a fused step (nothing reads the output back in this launch, and it leaves less to
-          // write back when the launch ends); plain in a trial, whose commit reads the missed rows back
-          if (kMode == kTrial) gr[c] = v[u];
-          else __builtin_nontemporal_store(v[u], gr + c);
-          if (hot_dst[u] >= 0) hotr[hot_dst[u]] = v[u];
-        }
-      }
-    }
-  }
+  rows_phase<kMode>(a, r, m, mtok, vict, gsrc, tid);
 
   if (tid == 0) {
     if (kMode != kTrial) a.step[r] = t + 1;
     a.miss[r] = m;
     a.status[r] = misc[kMiscStatus];
+  }
+}
+
+// Raw buffer access (gfx9 family): a per-request descriptor in scalar registers and a 32-bit byte offset per
+// lane. An offset at or past the descriptor's size reads 0 and writes nothing, so a lane's access is
+// predicated by its offset rather than by a branch around it.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+constexpr uint32_t kNoAccess = 0x80000000u;  // past every per-request array (each is below 2 GiB)
+
+__device__ __forceinline__ rsrc_t buf(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t ld32(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0); }
+__device__ __forceinline__ v2u ld64(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0); }
+__device__ __forceinline__ v4u ld128(rsrc_t r, uint32_t off) { return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0); }
+__device__ __forceinline__ void st16(uint32_t v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void st32(uint32_t v, rsrc_t r, uint32_t off) { __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0); }
+__device__ __forceinline__ void st128(v4u v, rsrc_t r, uint32_t off) { __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0); }
+
+// The direct-layout resolve (see the top of this file): kIPT selected ids per thread (position tid + u * 1024),
+// kSPT slots and LRU order positions per thread (one contiguous chunk, kSPT a multiple of 4). The host takes it
+// only where B is a multiple of 4 and the slot table, stamps and order list are 16-byte aligned, so every chunk
+// of four slots is one 16-byte access. Accesses that only some lanes make are predicated through their address:
+// a global one by a buffer offset out of range, an LDS store by the dummy words after the misc words.
+template <int kMode, bool kFifo, int kIPT, int kSPT>
+__global__ __launch_bounds__(kThreads) void resolve_direct_kernel(ResolveArgs a) {
+  static_assert(kSPT % 4 == 0, "slot chunks are whole groups of four");
+  constexpr int kQ = kSPT / 4;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const Layout& L = a.L;
+  int32_t* stok = (int32_t*)(smem + L.stok);
+  uint8_t* sflag = smem + L.sflag;           // 1: hit this step, 2: victim this step
+  uint32_t* sflagw = (uint32_t*)(smem + L.sflag);
+  uint32_t* mbits = (uint32_t*)(smem + L.mbits);  // missed ids (resident ids follow, at L.rbits)
+  uint16_t* mpre = (uint16_t*)(smem + L.mpre);
+  int32_t* vict = (int32_t*)(smem + L.vict);
+  int32_t* mtok = (int32_t*)(smem + L.mtok);
+  int32_t* gsrc = (int32_t*)(smem + L.gsrc);
+  int32_t* misc = (int32_t*)(smem + L.misc);
+  uint16_t* t2s = (uint16_t*)(smem + L.t2s);  // token -> slot that holds it (valid only where the slot agrees)
+  // LDS addresses a lane stores to when it has nothing to store
+  unsigned char* const dummy = smem + L.misc + 4 * kMiscDummy;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = blockIdx.x;
+  const int k = a.k, B = a.B, H = a.H, T = a.T;
+  const int W = (int)L.words;
+  const bool has_tail = a.tail0 != nullptr;
+  constexpr bool fifo = kFifo;
+  const int32_t t0 = has_tail ? a.tail0[r] : 0;
+  const int32_t t = a.step[r];
+  const size_t rk = (size_t)r * k, rB = (size_t)r * B, rH = (size_t)r * H;
+  const bool sources = kMode == kPlan && a.plan_sources != 0;
+  const bool gathers = kMode != kPlan && a.gather != nullptr;
+  const rsrc_t topk_b = buf(a.topk + rk, 4u * k);
+  const rsrc_t stok_b = buf(a.slot_tok + rB, 4u * B);
+  const rsrc_t ord_b = buf(a.order + rB, 2u * B);
+  const rsrc_t stamp_b = buf(a.stamp + rB, 4u * B);
+  const rsrc_t out_b = buf(a.out + rk, 4u * k);
+  const rsrc_t page_b = buf(a.page + rH, 4u * H);
+  const rsrc_t plan_b = buf(a.plan + 4 * rk, kMode == kPlan ? 16u * k : 0u);
+  int32_t* const rec = kMode == kTrial ? a.trial + (size_t)r * a.trial_words : nullptr;
+  const rsrc_t rec_b = buf(rec, kMode == kTrial ? (uint32_t)(4 * (kTrialHead + 4 * k)) : 0u);
+  const rsrc_t nord_b = kMode == kTrial ? buf(rec + kTrialHead + 4 * k, 2u * B) : ord_b;  // the new LRU order
+  const int s0 = tid * kSPT;  // this thread's slots and order positions: [s0, s0 + kSPT) within [0, B)
+  bool inq[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) inq[q] = s0 + 4 * q < B;
+
+  // ---- A: every global load of the step issued before any is consumed (the stamps only at the very end)
+  int32_t x[kIPT];
+#pragma unroll
+  for (int u = 0; u < kIPT; ++u) {
+    const int i = tid + u * kThreads;
+    const uint32_t v = ld32(topk_b, 4u * (uint32_t)i);  // past k: out of range
+    x[u] = i < k ? (int32_t)v : -1;
+  }
+  v4u yq[kQ], sq[kQ];
+  v2u oq[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) yq[q] = ld128(stok_b, 4u * (uint32_t)(s0 + 4 * q));
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) oq[q] = ld64(ord_b, 2u * (uint32_t)(s0 + 4 * q));
+  if (kMode != kTrial) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) sq[q] = ld128(stamp_b, 4u * (uint32_t)(s0 + 4 * q));
+  }
+  // scratch cleared while the loads are in flight: the missed-id and resident-id bitmaps (adjacent; at most
+  // two 16-byte stores per thread), and this chunk's slot flags
+  {
+    const int n16 = (int)((L.mpre - L.mbits) >> 4);
+    uint4* bm = reinterpret_cast<uint4*>(smem + L.mbits);
+    uint4* d16 = reinterpret_cast<uint4*>(dummy);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int q = tid + c * kThreads;
+      *(q < n16 ? bm + q : d16) = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  int32_t y[kSPT];
+  uint32_t o[kSPT];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    y[4 * q] = inq[q] ? (int32_t)yq[q].x : -1;
+    y[4 * q + 1] = inq[q] ? (int32_t)yq[q].y : -1;
+    y[4 * q + 2] = inq[q] ? (int32_t)yq[q].z : -1;
+    y[4 * q + 3] = inq[q] ? (int32_t)yq[q].w : -1;
+    o[4 * q] = oq[q].x & 0xffffu;
+    o[4 * q + 1] = oq[q].x >> 16;
+    o[4 * q + 2] = oq[q].y & 0xffffu;
+    o[4 * q + 3] = oq[q].y >> 16;
+    *reinterpret_cast<uint32_t*>(inq[q] ? (unsigned char*)(sflagw + (s0 >> 2) + q) : dummy) = 0u;
+    *reinterpret_cast<v4u*>(inq[q] ? (unsigned char*)(stok + s0 + 4 * q) : dummy) = yq[q];
+  }
+  // stage the slot table; each slot writes its index under its token (a slot with no valid token writes
+  // into the spare entry past the table)
+  int bad = 0;
+#pragma unroll
+  for (int u = 0; u < kSPT; ++u) {
+    const bool in = inq[u / 4];
+    bad |= in && (((uint32_t)y[u] + 1u > (uint32_t)H) | (o[u] >= (uint32_t)B));  // y in [-1, H), order < B
+    const bool tok = in && y[u] >= 0 && y[u] < H;
+    t2s[tok ? y[u] : H] = (uint16_t)(s0 + u);
+  }
+  {
+    const bool wbad = __ballot(bad) != 0ull;  // every lane takes part in the ballot
+    if (lane == 0) misc[kMiscWaveBad + wave] = wbad;
+  }
+  __syncthreads();  // (1)
+  if (any_wave_flag(misc + kMiscWaveBad, lane)) {
+    refuse_request<kMode>(a, r, tid);  // impossible state: leave the request untouched
+    return;
+  }
+
+  // ---- B: classify the ids and test each against the slot table from its own side. Every predicate is
+  // evaluated in full (bitwise, no short circuit) and every choice is a select, so no lane branches.
+  int st = 0;
+  bool cand[kIPT], res[kIPT], hit[kIPT];
+  uint32_t hs[kIPT];
+#pragma unroll
+  for (int u = 0; u < kIPT; ++u) {
+    // -1 is padding; outside [0, H), or at or past the tail start but outside the tail, is a bad id; inside
+    // the tail is resident; anything else is a candidate for the hot buffer
+    const int32_t xv = x[u];
+    const bool pad = xv == -1;
+    const bool in_h = (uint32_t)xv < (uint32_t)H;
+    const bool past = has_tail & (xv >= t0);
+    const bool in_t = (uint32_t)xv - (uint32_t)t0 < (uint32_t)T;  // exact in uint32 once x >= t0
+    const bool badid = !pad & (!in_h | (past & !in_t));
+    st |= badid ? kStatusBadId : 0;
+    res[u] = in_h & past & in_t;
+    cand[u] = in_h & !past;
+  }
+#pragma unroll
+  for (int u = 0; u < kIPT; ++u) hs[u] = t2s[cand[u] ? x[u] : 0];
+  int32_t held[kIPT];
+#pragma unroll
+  for (int u = 0; u < kIPT; ++u) held[u] = stok[hs[u] < (uint32_t)B ? hs[u] : 0u];
+  bool rep = false;
+  {
+    // one OR per id: a hit marks its slot's flag byte, a miss its bit among the missed ids, a resident id
+    // its bit in the tail window; finding it already set means the id is repeated. Byte offsets in LDS.
+    uint32_t off[kIPT], bit[kIPT], old[kIPT];
+#pragma unroll
+    for (int u = 0; u < kIPT; ++u) {
+      const uint32_t xv = (uint32_t)x[u], ri = xv - (uint32_t)t0;
+      hit[u] = cand[u] & (hs[u] < (uint32_t)B) & (held[u] == x[u]);
+      const uint32_t o_hit = L.sflag + (hs[u] & ~3u), b_hit = 1u << ((hs[u] & 3u) << 3);
+      const uint32_t o_miss = L.mbits + ((xv >> 5) << 2), b_miss = 1u << (xv & 31u);
+      const uint32_t o_res = L.rbits + ((ri >> 5) << 2), b_res = 1u << (ri & 31u);
+      uint32_t o = hit[u] ? o_hit : o_miss, b = hit[u] ? b_hit : b_miss;
+      o = res[u] ? o_res : o;
+      b = res[u] ? b_res : b;
+      off[u] = (cand[u] | res[u]) ? o : L.mbits;
+      bit[u] = (cand[u] | res[u]) ? b : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kIPT; ++u) old[u] = atomicOr(reinterpret_cast<uint32_t*>(smem + off[u]), bit[u]);
+#pragma unroll
+    for (int u = 0; u < kIPT; ++u) rep |= (old[u] & bit[u]) != 0u;
+  }
+  {
+    const bool wrep = __ballot(rep) != 0ull;  // every lane takes part in the ballots
+    const int wst = wave_or_bits(st);
+    if (lane == 0) {
+      misc[kMiscWaveRep + wave] = wrep;
+      misc[kMiscWaveSt + wave] = wst;
+    }
+  }
+  __syncthreads();  // (2)
+
+  const bool repeats = any_wave_flag(misc + kMiscWaveRep, lane);
+  if (repeats) {
+    // Rare: some id is selected twice. The lowest position holding it keeps it: the selected ids are ranked
+    // in a bitmap with prefix counts and every position bids for its id's rank, in the table's region (the
+    // table is dead now). Bits and flags set above are the same for every copy of an id, so only the losers
+    // change, and they only in this thread's registers.
+    uint32_t* sel = (uint32_t*)(smem + L.sel);
+    uint16_t* selpre = (uint16_t*)(smem + L.selpre);
+    int32_t* first = (int32_t*)(smem + L.first);
+    for (int w = tid; w < W; w += kThreads) sel[w] = 0u;
+    for (int q = tid; q < k; q += kThreads) first[q] = INT_MAX;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kIPT; ++u)
+      if (cand[u] || res[u]) atomicOr(&sel[x[u] >> 5], 1u << (x[u] & 31));
+    __syncthreads();
+    const int cw = (W + kThreads - 1) / kThreads, w0 = min(W, tid * cw), w1 = min(W, w0 + cw);
+    int cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(sel[w]);
+    int n_sel;
+    int run = block_excl_scan(cnt, misc + kMiscScanSel, lane, wave, &n_sel);
+    for (int w = w0; w < w1; ++w) {
+      selpre[w] = (uint16_t)run;
+      run += __popc(sel[w]);
+    }
+    __syncthreads();
+    int q[kIPT];
+#pragma unroll
+    for (int u = 0; u < kIPT; ++u) {
+      q[u] = 0;
+      if (cand[u] || res[u]) {
+        q[u] = (int)selpre[x[u] >> 5] + __popc(sel[x[u] >> 5] & below(x[u]));
+        atomicMin(&first[q[u]], tid + u * kThreads);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kIPT; ++u)
+      if ((cand[u] || res[u]) && first[q[u]] != tid + u * kThreads) cand[u] = res[u] = hit[u] = false;  // a repeat
+  }
+
+  // ---- C: ranks of the misses (ascending id) and of the non-hit slots in LRU order, in one scan
+  // (misses in the low 16 bits: m <= k <= 8192; candidates in the high 16 bits: <= B <= 8192). This thread's
+  // words of the missed-id bitmap: up to three (W <= 3072 for any direct layout).
+  const int cw = (W + kThreads - 1) / kThreads, w0 = tid * cw;
+  uint32_t mw[3];
+#pragma unroll
+  for (int e = 0; e < 3; ++e) {
+    const int w = w0 + e;
+    const bool inw = e < cw && w < W;
+    mw[e] = mbits[inw ? w : 0];
+    mw[e] = inw ? mw[e] : 0u;
+  }
+  int m, ncand;
+  {
+    const int cm = __popc(mw[0]) + __popc(mw[1]) + __popc(mw[2]);
+    uint32_t fl[kSPT];
+    int cc = 0;
+#pragma unroll
+    for (int u = 0; u < kSPT; ++u) {
+      fl[u] = inq[u / 4] ? (uint32_t)sflag[o[u]] : 1u;  // past the end: not a candidate
+      cc += !(fl[u] & 1u);
+    }
+    int tot;
+    const int pre = block_excl_scan(cm | (cc << 16), misc + kMiscScanRank, lane, wave, &tot);  // (3)
+    m = tot & 0xffff;
+    ncand = (int)((uint32_t)tot >> 16);
+    if (m > ncand) {
+      // more misses than free slots: only possible with a corrupt slot table
+      refuse_request<kMode>(a, r, tid);
+      return;
+    }
+    const uint32_t p0 = (uint32_t)(pre & 0xffff), p1 = p0 + __popc(mw[0]), p2 = p1 + __popc(mw[1]);
+#pragma unroll
+    for (int e = 0; e < 3; ++e) {
+      const int w = w0 + e;
+      const bool inw = e < cw && w < W;
+      *reinterpret_cast<uint16_t*>(inw ? (unsigned char*)(mpre + w) : dummy) = (uint16_t)(e == 0 ? p0 : e == 1 ? p1 : p2);
+    }
+    // LRU: the new order opens with the candidates that stay; FIFO: with every slot that stays (hits keep
+    // their place), position p moving up by the number of victims before it. A victim's evicted token leaves
+    // the page table here already, so these scattered stores start draining early (a plan records it for the
+    // copy, which updates the page table).
+    int runC = (int)((uint32_t)pre >> 16);
+#pragma unroll
+    for (int u = 0; u < kSPT; ++u) {
+      const int p = s0 + u;
+      const uint32_t slot = o[u];
+      const bool in = inq[u / 4];
+      const bool nonhit = in & !(fl[u] & 1u);
+      const bool isv = nonhit & (runC < m);
+      const uint32_t dv = (uint32_t)(dummy - smem);
+      *reinterpret_cast<int32_t*>(smem + (isv ? L.vict + 4u * (uint32_t)runC : dv)) = (int32_t)slot;
+      smem[isv ? L.sflag + slot : dv] = 2;
+      if (kMode == kFused) {
+        const int32_t yo = stok[isv ? slot : 0u];
+        st32(0xffffffffu, page_b, (isv & (yo >= 0)) ? 4u * (uint32_t)yo : kNoAccess);
+      } else if (kMode == kPlan) {
+        const int32_t yo = stok[isv ? slot : 0u];
+        st32((uint32_t)yo, plan_b, isv ? 4u * (uint32_t)(2 * k + runC) : kNoAccess);
+      }
+      const bool keep = fifo ? (in & !isv) : (nonhit & !isv);
+      const int np = fifo ? (nonhit ? p - m : p - min(m, runC)) : runC - m;
+      st16(slot, nord_b, keep ? 2u * (uint32_t)np : kNoAccess);
+      runC += nonhit ? 1 : 0;
+    }
+  }
+  __syncthreads();  // (4)
+
+  // ---- D: the j-th missed id takes the j-th victim: outputs, the new tokens' page entries (fused; a plan leaves
+  // them to the copy), the LDS slot table
+  {
+    bool mi[kIPT];
+    uint32_t mp[kIPT], mb[kIPT];
+#pragma unroll
+    for (int u = 0; u < kIPT; ++u) {
+      mi[u] = cand[u] & !hit[u];
+      const int w = mi[u] ? x[u] >> 5 : 0;
+      mp[u] = mpre[w];
+      mb[u] = mbits[w];
+    }
+    int j[kIPT], v[kIPT];
+#pragma unroll
+    for (int u = 0; u < kIPT; ++u) {
+      j[u] = mi[u] ? (int)mp[u] + __popc(mb[u] & below(x[u])) : 0;
+      v[u] = vict[j[u]];
+    }
+    int32_t yv[kIPT];
+    if (kMode == kTrial) {
+#pragma unroll
+      for (int u = 0; u < kIPT; ++u) yv[u] = stok[mi[u] ? v[u] : 0];
+    }
+#pragma unroll
+    for (int u = 0; u < kIPT; ++u) {
+      const int i = tid + u * kThreads;
+      const bool pos = i < k;
+      // the output: a miss's victim, a hit's slot, a resident id's ring row B + x mod T, else -1
+      int32_t ov = res[u] ? B + x[u] % (T > 0 ? T : 1) : -1;
+      ov = hit[u] ? (int32_t)hs[u] : ov;
+      ov = mi[u] ? v[u] : ov;
+      const int32_t g = mi[u] ? -2 - j[u] : ov;  // where the row comes from
+      st32((uint32_t)ov, out_b, pos ? 4u * (uint32_t)i : kNoAccess);
+      if (sources) st32((uint32_t)g, plan_b, pos ? 4u * (uint32_t)(3 * k + i) : kNoAccess);
+      if (gathers) *reinterpret_cast<int32_t*>(pos ? (unsigned char*)(gsrc + i) : dummy) = g;
+      if (kMode == kTrial) {
+        const uint32_t jo = mi[u] ? 4u * (uint32_t)(kTrialHead + j[u]) : kNoAccess;
+        st32((uint32_t)x[u], rec_b, jo);
+        st32((uint32_t)v[u], rec_b, jo + 4u * k);
+        st32((uint32_t)yv[u], rec_b, jo + 8u * k);
+        st32((uint32_t)i, rec_b, jo + 12u * k);
+      } else if (kMode == kFused) {
+        st32((uint32_t)v[u], page_b, mi[u] ? 4u * (uint32_t)x[u] : kNoAccess);
+      }
+      *reinterpret_cast<int32_t*>(mi[u] ? (unsigned char*)(stok + v[u]) : dummy) = x[u];  // one miss per victim
+      *reinterpret_cast<int32_t*>(mi[u] ? (unsigned char*)(mtok + j[u]) : dummy) = x[u];
+    }
+  }
+  // the slots used this step close the new order in slot order: hits and victims (LRU) or victims only
+  // (FIFO); the scan's barrier also publishes the LDS writes above
+  const int tail_start = fifo ? B - m : ncand - m;
+  auto used = [&](uint32_t f) { return fifo ? f == 2u : f != 0u; };
+  uint32_t fw[kQ];
+  {
+    int ch = 0;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      fw[q] = sflagw[inq[q] ? (s0 >> 2) + q : 0];
+      fw[q] = inq[q] ? fw[q] : 0u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) ch += used((fw[q] >> (8 * b)) & 0xffu);
+    }
+    int tot;
+    int pos = tail_start + block_excl_scan(ch, misc + kMiscScanTail, lane, wave, &tot);  // (5)
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const bool u = used((fw[q] >> (8 * b)) & 0xffu);
+        st16((uint32_t)(s0 + 4 * q + b), nord_b, u ? 2u * (uint32_t)pos : kNoAccess);  // pos < B for a permutation
+        pos += u ? 1 : 0;
+      }
+  }
+  // the stamps and the slot table written back as whole rows, 16 bytes per lane: the stamps of the used
+  // slots become t, the victims' entries their new tokens
+  if (kMode != kTrial) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const uint32_t f = fw[q];
+      v4u ns;
+      ns.x = used(f & 0xffu) ? (uint32_t)t : sq[q].x;
+      ns.y = used((f >> 8) & 0xffu) ? (uint32_t)t : sq[q].y;
+      ns.z = used((f >> 16) & 0xffu) ? (uint32_t)t : sq[q].z;
+      ns.w = used(f >> 24) ? (uint32_t)t : sq[q].w;
+      const uint32_t off = inq[q] ? 4u * (uint32_t)(s0 + 4 * q) : kNoAccess;
+      st128(ns, stamp_b, off);
+      st128(*reinterpret_cast<const v4u*>(stok + (inq[q] ? s0 + 4 * q : 0)), stok_b, off);
+    }
+  }
+  const int status = [&] {
+    int v = lane < kWaves ? misc[kMiscWaveSt + lane] : 0;
+    return wave_or_bits(v) | (repeats ? kStatusDupId : 0);
+  }();
+
+  if (kMode == kPlan) {
+#pragma unroll
+    for (int u = 0; u < kIPT; ++u) {
+      const int jj = tid + u * kThreads;
+      const bool in = jj < m;
+      const int32_t xt = mtok[in ? jj : 0], vt = vict[in ? jj : 0];
+      st32((uint32_t)xt, plan_b, in ? 4u * (uint32_t)jj : kNoAccess);
+      st32((uint32_t)vt, plan_b, in ? 4u * (uint32_t)(k + jj) : kNoAccess);
+    }
+    if (tid == 0) {
+      a.step[r] = t + 1;
+      a.miss[r] = m;
+      a.status[r] = status;
+    }
+    return;
+  }
+
+  if (kMode == kTrial && tid == 0) trial_header(a, r, m, tail_start, t);
+
+  // ---- E: rows (the block scan above ended with a barrier, so mtok and gsrc are visible)
+  rows_phase<kMode>(a, r, m, mtok, vict, gsrc, tid);
+
+  if (tid == 0) {
+    if (kMode != kTrial) a.step[r] = t + 1;
+    a.miss[r] = m;
+    a.status[r] = status;
   }
 }
 
@@ -742,8 +1188,21 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs a) {
   }
 }
 
+// The page-table updates of request r's plan: the evicted tokens leave it, the missed tokens point at their
+// slots (no token is both in one step). Thread t of n handles misses t, t + n, ...
+__device__ __forceinline__ void plan_page_updates(const CopyArgs& a, int r, int m, int t, int n) {
+  const int32_t* p = a.plan + (size_t)r * 4 * a.k;
+  int32_t* page = a.page + (size_t)r * a.H;
+  for (int j = t; j < m; j += n) {
+    const int32_t x = p[j], v = p[a.k + j], y = p[2 * a.k + j];
+    if (y >= 0 && y < a.H) page[y] = -1;
+    if (x >= 0 && x < a.H && v >= 0 && v < a.B) page[x] = v;
+  }
+}
+
 // Rows of a plan: workgroup (g, r) copies every gridDim.x-th group of 16-byte chunks of request r's
-// missed rows from the pinned host pool into their victim slots, one load in flight per thread.
+// missed rows from the pinned host pool into their victim slots, one load in flight per thread, and then its
+// share of the plan's page-table updates.
 __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
   const int r = blockIdx.y;
   const int m = a.miss[r];
@@ -751,7 +1210,7 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
   const int row16 = a.row16;
   const int total = m * row16;
   const size_t rk = (size_t)r * a.k;
-  const int32_t* ptok = a.plan + rk * 3;
+  const int32_t* ptok = a.plan + rk * 4;
   const int32_t* pslot = ptok + a.k;
   const v4u* hostr = a.host + (size_t)r * a.H * row16;
   v4u* hotr = a.hot + (size_t)r * a.B * row16;
@@ -762,12 +1221,14 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
     if (x >= 0 && x < a.H && s >= 0 && s < a.B)
       hotr[(size_t)s * row16 + q] = load_host(hostr + (size_t)x * row16 + q);
   }
+  plan_page_updates(a, r, m, blockIdx.x * blockDim.x + threadIdx.x, stride);
 }
 
 // A plan's rows and the gather of every selected row, in the gather kernel's tiles: workgroup (b, r) fills
 // positions [b*rows, b*rows + rows) of request r's gather output, each 16-byte chunk from where the plan says
 // the position's row is: a missed row from the host pool (also written to its victim slot), a hot slot, a tail
-// row, or zeros. The host loads spread over every workgroup of the chip rather than one per request.
+// row, or zeros. The host loads spread over every workgroup of the chip rather than one per request. The
+// page-table updates are shared out over the request's workgroups too.
 __global__ __launch_bounds__(kGatherThreads) void copy_gather_kernel(CopyArgs a) {
   const int r = blockIdx.y;
   const int i0 = blockIdx.x * a.rows;
@@ -775,9 +1236,9 @@ __global__ __launch_bounds__(kGatherThreads) void copy_gather_kernel(CopyArgs a)
   const int n = min(a.rows, k - i0) * row16;
   const int m = a.miss[r];
   const size_t rk = (size_t)r * k;
-  const int32_t* ptok = a.plan + rk * 3;
+  const int32_t* ptok = a.plan + rk * 4;
   const int32_t* pslot = ptok + k;
-  const int32_t* psrc = ptok + 2 * k + i0;
+  const int32_t* psrc = ptok + 3 * k + i0;
   const v4u* hostr = a.host + (size_t)r * a.H * row16;
   v4u* hotr = a.hot + (size_t)r * B * row16;
   const v4u* tailr = a.tail ? a.tail + (size_t)r * a.T * row16 : nullptr;
@@ -816,6 +1277,7 @@ __global__ __launch_bounds__(kGatherThreads) void copy_gather_kernel(CopyArgs a)
       if (slot_dst[u] >= 0) hotr[slot_dst[u]] = v[u];
     }
   }
+  if (m > 0 && m <= k) plan_page_updates(a, r, m, blockIdx.x * kGatherThreads + threadIdx.x, gridDim.x * kGatherThreads);
 }
 
 // Applies accepted trial records: the new LRU order, stamp t for the hit and victim slots (the new order's
@@ -1035,6 +1497,12 @@ hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes) {
       (const void*)resolve_kernel<kFused, false>, (const void*)resolve_kernel<kFused, true>,
       (const void*)resolve_kernel<kPlan, false>,  (const void*)resolve_kernel<kPlan, true>,
       (const void*)resolve_kernel<kTrial, false>, (const void*)resolve_kernel<kTrial, true>,
+      (const void*)resolve_direct_kernel<kFused, false, 2, 4>, (const void*)resolve_direct_kernel<kFused, true, 2, 4>,
+      (const void*)resolve_direct_kernel<kPlan, false, 2, 4>,  (const void*)resolve_direct_kernel<kPlan, true, 2, 4>,
+      (const void*)resolve_direct_kernel<kTrial, false, 2, 4>, (const void*)resolve_direct_kernel<kTrial, true, 2, 4>,
+      (const void*)resolve_direct_kernel<kFused, false, 8, 8>, (const void*)resolve_direct_kernel<kFused, true, 8, 8>,
+      (const void*)resolve_direct_kernel<kPlan, false, 8, 8>,  (const void*)resolve_direct_kernel<kPlan, true, 8, 8>,
+      (const void*)resolve_direct_kernel<kTrial, false, 8, 8>, (const void*)resolve_direct_kernel<kTrial, true, 8, 8>,
   };
   hipError_t e = hipSuccess;
   for (const void* f : resolve_variants) {
@@ -1047,13 +1515,23 @@ hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes) {
                              (int)rebuild_bytes);
 }
 
+template <int kMode, bool kFifo>
+static void launch_mode_policy(const ResolveArgs& a, hipStream_t s) {
+  const dim3 grid(a.R), block(kThreads);
+  if (!a.L.direct) hipLaunchKernelGGL((resolve_kernel<kMode, kFifo>), grid, block, a.L.total, s, a);
+  else if (a.k <= 2 * kThreads && a.B <= 4 * kThreads)
+    hipLaunchKernelGGL((resolve_direct_kernel<kMode, kFifo, 2, 4>), grid, block, a.L.total, s, a);
+  else hipLaunchKernelGGL((resolve_direct_kernel<kMode, kFifo, 8, 8>), grid, block, a.L.total, s, a);
+}
+
 template <int kMode>
 static void launch_mode(const ResolveArgs& a, hipStream_t s) {
-  if (a.policy == 1) hipLaunchKernelGGL((resolve_kernel<kMode, true>), dim3(a.R), dim3(kThreads), a.L.total, s, a);
-  else hipLaunchKernelGGL((resolve_kernel<kMode, false>), dim3(a.R), dim3(kThreads), a.L.total, s, a);
+  if (a.policy == 1) launch_mode_policy<kMode, true>(a, s);
+  else launch_mode_policy<kMode, false>(a, s);
 }
 
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s) {
+  if (a.L.direct && (a.B > kDirectMaxSlots || a.k > 8 * kThreads)) return hipErrorInvalidValue;
   if (a.trial) launch_mode<kTrial>(a, s);
   else if (a.plan) launch_mode<kPlan>(a, s);
   else launch_mode<kFused>(a, s);

@@ -19,6 +19,7 @@ _lib = None
 HS_OK, HS_E_INVALID, HS_E_NOMEM, HS_E_HIP, HS_E_STATE = 0, -1, -2, -3, -4
 HS_STATUS_BAD_ID, HS_STATUS_DUP_ID, HS_STATUS_BAD_STATE, HS_STATUS_STALE = 1, 2, 4, 8
 HS_EVICT_LRU, HS_EVICT_FIFO = 0, 1
+HS_PLAN_ROW_SOURCES = 1
 
 EXPORTED = ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
             "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_offload", "hs_advance_tail", "hs_gather",
@@ -49,7 +50,7 @@ class HsSizes(ctypes.Structure):
                 ("topk_bytes", ctypes.c_uint64), ("out_bytes", ctypes.c_uint64), ("gather_bytes", ctypes.c_uint64),
                 ("plan_bytes", ctypes.c_uint64), ("trial_bytes", ctypes.c_uint64), ("lds_bytes", ctypes.c_uint32),
                 ("lds_bytes_launch", ctypes.c_uint32), ("lds_bytes_launch_gather", ctypes.c_uint32),
-                ("token_slot_table", ctypes.c_uint32)]
+                ("token_slot_table", ctypes.c_uint32), ("lds_bytes_rank", ctypes.c_uint32)]
 
 
 def library_path() -> str:
@@ -74,7 +75,7 @@ def lib():
         L.hs_bind_device.argtypes = [vp, ctypes.POINTER(HsDeviceViews)]
         L.hs_reset.argtypes = [vp, vp, i32, vp]
         L.hs_resolve.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
-        L.hs_plan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        L.hs_plan.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp]
         L.hs_copy.argtypes = [vp, vp, vp, vp, vp]
         L.hs_trial.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.hs_commit.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -184,9 +185,10 @@ def hs_resolve(ctx, topk, tail0, out, miss, status, gather=None, stream=None) ->
                             _stream(stream)))
 
 
-def hs_plan(ctx, topk, tail0, out, miss, status, plan, stream=None) -> None:
+def hs_plan(ctx, topk, tail0, out, miss, status, plan, stream=None, row_sources: bool = False) -> None:
+    """row_sources: also record each position's row source, which a gathering hs_copy of this plan needs."""
     _check(lib().hs_plan(ctx, _ptr(topk), _ptr(tail0), _ptr(out), _ptr(miss), _ptr(status), _ptr(plan),
-                         _stream(stream)))
+                         HS_PLAN_ROW_SOURCES if row_sources else 0, _stream(stream)))
 
 
 def hs_copy(ctx, plan, miss, gather=None, stream=None) -> None:
@@ -281,7 +283,7 @@ class SwapIn:
 
     def plan_buffer(self):
         import torch
-        return torch.empty((self.R, 3, self.k), dtype=torch.int32, device=self.device)
+        return torch.empty((self.R, 4, self.k), dtype=torch.int32, device=self.device)
 
     def close(self) -> None:
         if self.ctx:

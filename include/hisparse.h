@@ -70,15 +70,17 @@ extern "C" {
  * Hierarchical Memory", section 3 launch scripts: top_k 2048,
  * device_buffer_size 4096 or 6144, host_to_device_ratio 8 or 10).
  * Beyond the per-field ranges, a shape is accepted only if one resolve
- * workgroup's LDS (hs_sizes.lds_bytes, about 21k + 7B + 14 * ceil(H / 32)
- * bytes, plus 4k more where that still fits, which saves the kernel a pass)
- * fits in 159 KiB, and the host pool (R x H x row_bytes) in 2^56 bytes;
- * hs_required_sizes and hs_create return HS_E_INVALID otherwise. Where a
- * uint16 token -> slot entry for each of the H host rows fits beside the
- * rest (about 13k + 7B + 14 * ceil(H / 32) + 2H bytes, 4k more for a launch
- * with a gather output), a launch uses that larger layout, up to 159 KiB,
- * and skips ranking the selected ids (hs_sizes.lds_bytes_launch,
- * .lds_bytes_launch_gather and .token_slot_table report which launches do).
+ * workgroup's LDS fits in 159 KiB for launches with and without a gather
+ * output, and the host pool (R x H x row_bytes) in 2^56 bytes;
+ * hs_required_sizes and hs_create return HS_E_INVALID otherwise. A launch
+ * takes one of two layouts. Where a uint16 token -> slot entry for each of
+ * the H host rows fits (the direct layout: about 8k + 8B + 6 * ceil(H / 32)
+ * + max(2H, 6 * ceil(H / 32) + 4k) bytes, 4k more with a gather output, and
+ * B <= 8192), it tests each selected id against the slot table directly.
+ * Elsewhere it ranks the selected ids in bitmaps over token ids (the rank
+ * layout: about 21k + 7B + 10 * ceil(H / 32) bytes, plus 4k more where that
+ * still fits, which saves the kernel a pass; at k = 2048 and B = 4096 that
+ * allows about 290,000 host rows). hs_sizes reports the bytes of each.
  */
 typedef struct hs_config {
   int32_t num_requests;       /* R, 1 .. 65535 */
@@ -127,14 +129,15 @@ typedef struct hs_sizes {
   uint64_t topk_bytes;       /* [R][k] int32 input of one step */
   uint64_t out_bytes;        /* [R][k] int32 output of one step */
   uint64_t gather_bytes;     /* [R][k][row_bytes] gather output */
-  uint64_t plan_bytes;       /* [R][3][k] int32 plan of hs_plan (miss list and row sources) */
+  uint64_t plan_bytes;       /* [R][4][k] int32 plan of hs_plan (miss list, evicted tokens, row sources) */
   uint64_t trial_bytes;      /* trial records of hs_trial / hs_commit */
-  uint32_t lds_bytes;        /* LDS one resolve workgroup needs at least */
+  uint32_t lds_bytes;        /* LDS a resolve workgroup of this shape takes at most (the larger of the two below) */
   uint32_t lds_bytes_launch;        /* LDS a resolve / plan launch without a gather output takes (device
-                                       allowing 159 KiB): the token -> slot layout where it fits */
+                                       allowing 159 KiB): the direct layout where it fits, else the rank layout */
   uint32_t lds_bytes_launch_gather; /* the same for a launch with a gather output (fused gather, trial) */
-  uint32_t token_slot_table;        /* bit 0: launches without a gather output use the token -> slot table;
+  uint32_t token_slot_table;        /* bit 0: launches without a gather output use the direct layout;
                                        bit 1: launches with one do */
+  uint32_t lds_bytes_rank;          /* LDS of the rank layout of this shape (whether or not launches take it) */
 } hs_sizes;
 
 typedef struct hs_ctx hs_ctx;
@@ -185,19 +188,26 @@ int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32
  * the swap-in I/O as the way to cut its cost ("HiSparse: Turbocharging Sparse Attention with Hierarchical
  * Memory", section 4 future work; 「HiSparse：階層化メモリシステムによるスパースアテンションの加速」, section
  * 「今後の展望」).
- * hs_plan does everything hs_resolve does except moving rows: outputs, page table, slot table, stamps and
- * step counters are final when it completes; d_plan [R][3][k] int32 receives, for request r, the missed
- * tokens in ascending id order (d_plan[r][0][0..m)), their slots (d_plan[r][1][0..m)) and, for every
- * position i of the selection, where its row is (d_plan[r][2][i]: a slot in [0, B), B + a tail row, -1 for
- * none, or -2 - j for the j-th miss).
- * hs_copy then copies those rows from the host pool into the hot buffer. With d_gather (nullable,
- * [R][k][row_bytes], 16-byte aligned) it also writes every selected row there, as hs_resolve's fused gather
- * does, in workgroups spread over the whole chip (the missed rows straight from the host pool). Until it
- * completes, the hot rows of this step's new slots are stale. Two plans may run back to back, but the copy
- * of a step must complete before the copy of the next step and before anything reads the hot rows.
+ * hs_plan makes every decision of the step: outputs, slot table, stamps, LRU order and step counters are
+ * final when it completes. d_plan [R][4][k] int32 receives, for request r, the missed tokens in ascending id
+ * order (d_plan[r][0][0..m)), their slots (d_plan[r][1][0..m)), the tokens those slots held before (d_plan[r][2]
+ * [0..m), -1 for an empty slot) and, with flags HS_PLAN_ROW_SOURCES, for every position i of the selection,
+ * where its row is (d_plan[r][3][i]: a slot in [0, B), B + a tail row, -1 for none, or -2 - j for the j-th
+ * miss); without it d_plan[r][3] is not written. Unknown flag bits are refused (HS_E_INVALID).
+ * hs_copy then moves the rows and publishes the step in the page table: each missed row is copied from the
+ * host pool into its slot, the evicted tokens' page entries become -1 and the missed tokens' entries their
+ * slots (the page table is not read on the decode path, so its scattered updates ride with the link-bound
+ * copy instead of the plan). With d_gather (nullable, [R][k][row_bytes], 16-byte aligned) it also writes
+ * every selected row there, as hs_resolve's fused gather does, in workgroups spread over the whole chip (the
+ * missed rows straight from the host pool); that needs a plan made with HS_PLAN_ROW_SOURCES (other plans give
+ * undefined rows, never an access out of bounds). Until hs_copy completes, the hot rows of this step's new
+ * slots are stale and the page table does not show the step. Two plans may run back to back, but the copy of
+ * a step must complete before the copy of the next step and before any call other than hs_plan reads or
+ * writes the context's state.
  */
+#define HS_PLAN_ROW_SOURCES 1 /* hs_plan flag: also record each position's row source (for a gathering hs_copy) */
 int hs_plan(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
-            int32_t* d_status, int32_t* d_plan, void* stream);
+            int32_t* d_status, int32_t* d_plan, int32_t flags, void* stream);
 int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* d_gather, void* stream);
 
 /*

@@ -94,23 +94,46 @@ def test_sizes_of_the_workloads():
         assert s.hot_bytes == w.num_requests * w.buffer_slots * w.row_bytes
 
 
+MISC = 4 * (8 * 16 + 8)  # the scan and flag words every layout carries
+
+
+def _words(H):
+    return (H + 31) // 32
+
+
 def test_lds_layout_takes_the_missed_token_array_where_it_fits():
-    """One resolve workgroup needs about 21k + 7B + 14 ceil(H/32) bytes of LDS; the missed tokens get 4k bytes
-    of their own only while the total stays within 159 KiB (near the limit they share the rank-to-slot table)."""
+    """The rank layout needs about 21k + 7B + 10 ceil(H/32) bytes of LDS; the missed tokens get 4k bytes of their
+    own only while the total stays within 159 KiB (near the limit they share the rank-to-slot table)."""
     def base(k, B, H):
-        return 21 * k + 7 * B + 14 * ((H + 31) // 32)
+        return 21 * k + 7 * B + 10 * _words(H) + MISC
 
     def lds(k, B, H):
-        return hm.hs_required_sizes(hm.config(2, k, B, 0.0, 1152, H)).lds_bytes
+        return hm.hs_required_sizes(hm.config(2, k, B, 0.0, 1152, H)).lds_bytes_rank
 
-    for k, B, H in ((2048, 4096, 40960), (2048, 4096, 131072), (256, 512, 4096), (2048, 8192, 120000)):
+    for k, B, H in ((2048, 4096, 40960), (2048, 4096, 131072), (256, 512, 4096), (2048, 8192, 131072),
+                    (2048, 4096, 262144)):
         extra = lds(k, B, H) - base(k, B, H)
-        assert 4 * k <= extra <= 4 * k + 512, (k, B, H, extra)
+        assert 4 * k <= extra <= 4 * k + 256, (k, B, H, extra)
         assert lds(k, B, H) <= 159 * 1024
-    for k, B, H in ((2048, 8192, 131072), (4096, 4096, 100000)):
+    for k, B, H in ((2048, 8192, 180000), (4096, 4096, 150000)):
         extra = lds(k, B, H) - base(k, B, H)
-        assert 0 <= extra <= 512, (k, B, H, extra)
+        assert 0 <= extra <= 256, (k, B, H, extra)
         assert lds(k, B, H) + 4 * k > 159 * 1024
+
+
+def test_context_length_limit_of_the_rank_layout():
+    """At k = 2048 and B = 4096 the rank layout holds about 290,000 host rows per request (262,144 is accepted);
+    past 159 KiB the shape is refused."""
+    ok = hm.hs_required_sizes(hm.config(2, 2048, 4096, 0.0, 64, 262144))
+    assert ok.lds_bytes <= 159 * 1024 and ok.token_slot_table == 0
+    limit = 159 * 1024 - (21 * 2048 + 7 * 4096 + MISC)
+    h_max = (limit // 10) * 32
+    assert 280000 < h_max < 300000
+    hm.hs_required_sizes(hm.config(2, 2048, 4096, 0.0, 64, h_max - 4096))
+    for H in (h_max + 32 * 64, 1 << 20):
+        with pytest.raises(hm.HiSparseError) as err:
+            hm.hs_required_sizes(hm.config(2, 2048, 4096, 0.0, 64, H))
+        assert err.value.code == hm.HS_E_INVALID and "LDS" in str(err.value)
 
 
 def test_binding_refuses_host_tensors():
@@ -138,19 +161,22 @@ def test_build_script_loads_without_the_built_library():
 
 
 def test_token_slot_table_where_it_fits():
-    """Launches take a uint16 token -> slot entry per host row where it fits beside the rest in 159 KiB (about
-    13k + 7B + 14 ceil(H/32) + 2H bytes, 4k more with a gather output); elsewhere they keep the rank layout."""
+    """Launches take the direct layout (a uint16 token -> slot entry per host row) where it fits in 159 KiB and
+    B <= 8192: about 8k + 8B + 6 ceil(H/32) + max(2H, 6 ceil(H/32) + 4k) bytes, 4k more with a gather output;
+    elsewhere the rank layout."""
     cap = 159 * 1024
-    # (k, B, H, expected bits): 256-request shape without a gather output only, 32-request and single-request
-    # shapes both, hybrid and sweep shapes neither
-    cases = ((2048, 4096, 40960, 1), (2048, 4096, 33024, 3), (256, 512, 4096, 3), (2048, 4096, 131072, 0),
-             (2048, 2048, 65536, 0), (2048, 6144, 65536, 0))
-    for k, B, H, bits in cases:
-        s = hm.hs_required_sizes(hm.config(2, k, B, 0.0, 1152, H))
+    # (k, B, H, T, expected bits): 256-request, 32-request and single-request shapes both ways, hybrid and sweep
+    # shapes neither, a buffer past the direct kernel's 8192 slots neither
+    cases = ((2048, 4096, 40960, 0, 3), (2048, 4096, 33024, 0, 3), (256, 512, 4096, 0, 3), (2048, 4096, 131072, 8192, 0),
+             (2048, 2048, 65536, 0, 0), (2048, 6144, 65536, 0, 0), (64, 9000, 4096, 0, 0), (2048, 8192, 8192, 100, 3))
+    for k, B, H, T, bits in cases:
+        s = hm.hs_required_sizes(hm.config(2, k, B, 0.0, 1152, H, T))
         assert s.token_slot_table == bits, (k, B, H, s.token_slot_table)
+        W = _words(H)
         for bit, got, extra in ((1, s.lds_bytes_launch, 0), (2, s.lds_bytes_launch_gather, 4 * k)):
             if bits & bit:
-                est = 13 * k + 7 * B + 14 * ((H + 31) // 32) + 2 * H + extra
-                assert est <= got <= est + 512 and got <= cap, (k, B, H, bit, got, est)
+                est = 8 * k + 4 * B + 4 * ((B + 3) // 4) + 6 * W + 4 * ((T + 31) // 32) + MISC + max(2 * H, 6 * W + 4 * k) + extra
+                assert est <= got <= est + 256 and got <= cap, (k, B, H, bit, got, est)
             else:
-                assert got == s.lds_bytes, (k, B, H, bit, got, s.lds_bytes)
+                assert got == s.lds_bytes_rank, (k, B, H, bit, got, s.lds_bytes_rank)
+        assert s.lds_bytes == max(s.lds_bytes_launch, s.lds_bytes_launch_gather)

@@ -88,6 +88,68 @@ def test_random_shapes(seed):
     p.close()
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_rank_layout(seed):
+    """Small random k and B with a long context (H >= 82,000: no room for a token -> slot table), so every
+    launch takes the rank layout; ids drawn from a window of about 3B tokens so that slots are hit, with
+    padding, bad and repeated ids, a device tail on some seeds, FIFO on others, with and without the gather."""
+    import hierarchical_memory_amd as hm
+    rng = np.random.default_rng(20_000 + seed)
+    k = int(rng.integers(1, 300))
+    B = int(rng.integers(k, 3 * k + 2))
+    H = int(rng.integers(82_000, 120_000))
+    T = int(rng.integers(1, 64)) if seed % 3 == 0 else 0
+    rb = int(rng.choice([16, 48, 1152]))
+    R = int(rng.integers(1, 12))
+    policy, gather, steps = seed % 2, bool(seed % 4 < 2), 6
+    sizes = hm.hs_required_sizes(hm.config(R, k, B, 0.0, rb, H, T, policy))
+    assert sizes.token_slot_table == 0
+    lo = int(rng.integers(0, H - 3 * B - 8))
+    ids = np.empty((R, steps, k), np.int32)
+    for r in range(R):
+        for t in range(steps):
+            row = (lo + rng.choice(3 * B, size=k, replace=False)).astype(np.int32)
+            weird = rng.random(k) < 0.05
+            row[weird] = rng.integers(-3, H + 3, size=int(weird.sum()))
+            ids[r, t] = row
+    log(f"[rank shape {seed}] R={R} k={k} B={B} H={H} T={T} rb={rb} policy={policy} gather={gather}")
+    w = workload.SINGLE_4K.with_(name=f"rank_{seed}", num_requests=R, top_k=k, buffer_slots=B, host_rows=H, L0=H,
+                                 tail_tokens=T, row_elems=rb // 2, steps=steps, fused_gather=gather)
+    tail0 = (lo + rng.integers(0, 3 * B, size=R)).astype(np.int32) if T else None
+    p = Pair(w, ids=ids, tail0=tail0, gather=gather, policy=policy)
+    p.run(check_every=1)
+    p.close()
+
+
+def test_context_of_262144_tokens():
+    """A 262,144-token context at k = 2048, B = 4096 (the rank layout, about 150 KiB of LDS): fused resolve with a
+    gather, then plan + copy, step by step against the oracle, with a repeated id on odd steps."""
+    import hierarchical_memory_amd as hm
+    H = 262144
+    w = workload.SINGLE_4K.with_(name="context_262144", num_requests=3, top_k=2048, buffer_slots=4096, host_rows=H,
+                                 L0=H, window=12000, row_elems=32, steps=8, fused_gather=True)
+    sizes = hm.hs_required_sizes(hm.config(3, 2048, 4096, 0.0, 64, H))
+    assert sizes.token_slot_table == 0 and sizes.lds_bytes <= 159 * 1024
+    ids = workload.streams(w)
+    ids[:, 1::2, 9] = ids[:, 1::2, 4]
+    p = Pair(w, ids=ids, gather=True)
+    p.run(check_every=1)
+    p.close()
+    p = Pair(w, ids=ids)
+    plan = p.sw.plan_buffer()
+    out, miss, status, _ = p.outs
+    for t in range(w.steps):
+        step_ids = p.ids[:, t]
+        hm.hs_plan(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(step_ids)).cuda(), None, out, miss, status, plan)
+        hm.hs_copy(p.sw.ctx, plan, miss)
+        o_out, o_miss, o_status, _ = p.o.step(step_ids[p.sample])
+        assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+        assert (status.cpu().numpy() == o_status).all()
+        p.t += 1
+        p.check_state()
+    p.close()
+
+
 def test_single_request_full():
     p = Pair(workload.SINGLE_4K, gather=True)
     p.run(check_every=1)
@@ -180,7 +242,7 @@ def test_maximum_request_count():
     out, miss, status, g = p.outs
     plan = p.sw.plan_buffer()
     topk = torch.from_numpy(np.ascontiguousarray(p.ids[:, 1])).cuda()
-    hm.hs_plan(p.sw.ctx, topk, None, out, miss, status, plan)
+    hm.hs_plan(p.sw.ctx, topk, None, out, miss, status, plan, row_sources=True)
     hm.hs_copy(p.sw.ctx, plan, miss, g)
     o_out, o_miss, _, o_g = p.o.step(p.ids[:, 1], gather=True)
     assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
@@ -352,14 +414,14 @@ def test_largest_shape_that_fits_lds():
 
 
 def test_shared_missed_token_array_near_the_lds_limit():
-    """At k = 2048, B = 8192, H = 131072 a separate missed-token array would pass 159 KiB of LDS, so the missed
+    """At k = 2048, B = 8192, H = 180000 a separate missed-token array would pass 159 KiB of LDS, so the missed
     tokens share the rank-to-slot table and the kernel keeps its settling pass: steps without and with repeated
     ids, fused and through plan + copy."""
     import hierarchical_memory_amd as hm
-    s = hm.hs_required_sizes(hm.config(2, 2048, 8192, 0.0, 1152, 131072))
-    assert s.lds_bytes + 4 * 2048 > 159 * 1024
+    s = hm.hs_required_sizes(hm.config(2, 2048, 8192, 0.0, 1152, 180000))
+    assert s.token_slot_table == 0 and s.lds_bytes_rank + 4 * 2048 > 159 * 1024
     w = workload.SINGLE_4K.with_(name="wide_shared", num_requests=2, top_k=2048, buffer_slots=8192,
-                                 host_rows=131072, L0=131072, window=20000, steps=8)
+                                 host_rows=180000, L0=180000, window=20000, steps=8)
     ids = workload.streams(w)
     ids[:, 1::2, 7] = ids[:, 1::2, 3]  # odd steps repeat an id
     p = Pair(w, ids=ids)
@@ -381,15 +443,15 @@ def test_shared_missed_token_array_near_the_lds_limit():
     p.close()
 
 
-@pytest.mark.parametrize("base,bits", [(workload.CONC_256, 1), (workload.GROW_32, 3)], ids=["256req_shape", "32req_shape"])
-def test_token_slot_table_beside_the_rank_path(base, bits):
-    """At the 256-request shape (k = 2048, B = 4096, H = 40960) a launch without a gather output has LDS for a
-    token -> slot entry per host row, so hit slots write their index under their token and the selected ids are
-    not ranked; a request whose selection repeats an id ranks them instead, in the same launch. With a gather
-    output the table does not fit there and every request ranks; at the 32-request shape (H = 33024) it fits with
-    one too. Requests 1 and 3 repeat an id on odd steps; fused without and with a gather, and plan + copy, step
-    by step against the oracle."""
+@pytest.mark.parametrize("base", [workload.CONC_256, workload.GROW_32], ids=["256req_shape", "32req_shape"])
+def test_direct_layout_with_repeated_ids(base):
+    """At the 256- and 32-request shapes every launch takes the direct layout (a token -> slot entry per host
+    row): each selected id is tested against the slot table from its own side. A request whose selection repeats
+    an id ranks its ids in the table's region instead, so the lowest position keeps the id. Requests 1 and 3
+    repeat an id on odd steps; fused without and with a gather, and plan + copy, step by step against the
+    oracle."""
     import hierarchical_memory_amd as hm
+    bits = 3
     w = base.with_(name=base.name + "_4req", num_requests=4, steps=8)
     sizes = hm.hs_required_sizes(hm.config(w.num_requests, w.top_k, w.buffer_slots, 0.0, w.row_bytes, w.host_rows))
     assert sizes.token_slot_table == bits
@@ -477,7 +539,7 @@ def test_plan_then_copy_with_gather(k, B, H, T, rb, policy):
     for t in range(steps):
         topk = torch.from_numpy(np.ascontiguousarray(ids[:, t])).cuda()
         g.fill_(0xCD)
-        hm.hs_plan(p.sw.ctx, topk, p.tail0_dev, out, miss, status, plan)
+        hm.hs_plan(p.sw.ctx, topk, p.tail0_dev, out, miss, status, plan, row_sources=True)
         hm.hs_copy(p.sw.ctx, plan, miss, g)
         o_out, o_miss, o_st, o_g = p.o.step(ids[:, t], p.tail0, gather=True)
         assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
@@ -544,7 +606,7 @@ def test_copy_with_gather_overlapped_on_second_stream():
         if copied[b] is not None:
             copied[b].synchronize()  # the copy of step t - 2 is done: check its rows, then reuse its buffers
             assert (gathers[b].cpu().numpy() == expected[b]).all(), f"step {t - 2}: gathered rows differ"
-        hm.hs_plan(p.sw.ctx, topk_all[t], p.tail0_dev, out, misses[b], status, plans[b], main)
+        hm.hs_plan(p.sw.ctx, topk_all[t], p.tail0_dev, out, misses[b], status, plans[b], main, row_sources=True)
         planned = torch.cuda.Event()
         planned.record(main)
         side.wait_event(planned)

@@ -95,7 +95,7 @@ def test_random_call_sequences(seed):
             if op in ("resolve", "resolve_gather"):
                 hm.hs_resolve(ctx, topk, p.tail0_dev, out, miss, status, g if gather else None)
             elif op in ("plan_copy", "plan_copy_gather"):
-                hm.hs_plan(ctx, topk, p.tail0_dev, out, miss, status, plan)
+                hm.hs_plan(ctx, topk, p.tail0_dev, out, miss, status, plan, row_sources=gather)
                 hm.hs_copy(ctx, plan, miss, g if gather else None)
             else:
                 hm.hs_trial(ctx, topk, p.tail0_dev, out, miss, status, g, trial)
