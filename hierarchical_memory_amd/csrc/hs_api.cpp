@@ -8,7 +8,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
+#include <vector>
 
 struct hs_ctx {
   hs_config cfg;
@@ -29,6 +31,11 @@ struct hs_ctx {
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Device address of the static plan array of each device (hs_step_static), taken once per device by the first
+// hs_create made while that device is current.
+std::mutex g_static_plan_mu;
+std::vector<void*> g_static_plan;
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -191,6 +198,16 @@ int hs_create(const hs_config* cfg, hs_ctx** out) {
   // the most any context may use, so a later context of a smaller shape cannot lower it under this one.
   e = hs::set_lds_limits(cap, cap);
   if (e != hipSuccess) return hip_fail(e, "hipFuncSetAttribute(resolve kernel LDS)");
+  {
+    std::lock_guard<std::mutex> lock(g_static_plan_mu);
+    if ((int)g_static_plan.size() <= dev) g_static_plan.resize((size_t)dev + 1, nullptr);
+    if (!g_static_plan[(size_t)dev]) {
+      void* p = nullptr;
+      e = hs::static_plan_address(&p);
+      if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(static plan)");
+      g_static_plan[(size_t)dev] = p;
+    }
+  }
 
   hs_ctx* ctx = new (std::nothrow) hs_ctx();
   if (!ctx) return fail(HS_E_NOMEM, "out of host memory for the context");
@@ -439,6 +456,30 @@ int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* d_g
   hipError_t e = hs::launch_copy(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "copy launch");
   return ok();
+}
+
+int hs_step_static(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
+                   int32_t* d_status, void* d_gather, void* stream) {
+  int rc = check_ready(ctx);
+  if (rc) return rc;
+  const uint64_t need = (uint64_t)ctx->cfg.num_requests * 4ull * (uint64_t)ctx->cfg.top_k * 4ull;
+  if (need > hs::kStaticPlanBytes)
+    return fail(HS_E_INVALID,
+                "the plan of %d requests x top_k %d takes %llu bytes, more than the %llu of the static plan; use "
+                "hs_plan and hs_copy with a plan buffer",
+                ctx->cfg.num_requests, ctx->cfg.top_k, (unsigned long long)need,
+                (unsigned long long)hs::kStaticPlanBytes);
+  void* plan = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_static_plan_mu);
+    if ((size_t)ctx->device < g_static_plan.size()) plan = g_static_plan[(size_t)ctx->device];
+  }
+  if (!plan) return fail(HS_E_STATE, "no static plan address for device %d", ctx->device);
+  if (d_gather && !aligned(d_gather, 16)) return fail(HS_E_INVALID, "gather output is not 16-byte aligned");
+  rc = resolve_common(ctx, d_topk, d_tail0, d_out, d_miss, d_status, nullptr, (int32_t*)plan,
+                      d_gather ? HS_PLAN_ROW_SOURCES : 0, nullptr, stream);
+  if (rc) return rc;
+  return hs_copy(ctx, (const int32_t*)plan, d_miss, d_gather, stream);
 }
 
 int hs_gather(hs_ctx* ctx, const int32_t* d_out, void* d_gather, void* stream) {

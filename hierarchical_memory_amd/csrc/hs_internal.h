@@ -229,6 +229,11 @@ struct GatherArgs {
   v4u* gather;
 };
 
+// The plan of hs_step_static lives in a file-scope device array of this many bytes (one copy per device, held
+// until the process ends); static_plan_address gives its device address on the current device.
+constexpr uint64_t kStaticPlanBytes = 8ull << 20;
+hipError_t static_plan_address(void** ptr);
+
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s);
 hipError_t launch_reset(const ResetArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);

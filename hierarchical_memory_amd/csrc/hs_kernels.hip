@@ -1379,6 +1379,12 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   }
 }
 
+// The plan of hs_step_static (the split step in one call, for callers that cannot allocate): kernels reach it
+// only through the device address static_plan_address returns, never through its name in host code.
+static __device__ __align__(256) int32_t scratch[kStaticPlanBytes / 4];
+
+hipError_t static_plan_address(void** ptr) { return hipGetSymbolAddress(ptr, HIP_SYMBOL(scratch)); }
+
 hipError_t launch_commit(const CommitArgs& a, hipStream_t s) {
   const size_t lds = (size_t)((a.B + 3) & ~3) + 8 * (size_t)a.k;  // flags, then slots and positions
   hipLaunchKernelGGL(commit_kernel, dim3(a.R), dim3(1024), lds, s, a);

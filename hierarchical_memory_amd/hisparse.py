@@ -23,7 +23,8 @@ HS_PLAN_ROW_SOURCES = 1
 
 EXPORTED = ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
             "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_offload", "hs_advance_tail", "hs_gather",
-            "hs_rebuild_order", "hs_destroy", "hs_last_error")
+            "hs_rebuild_order", "hs_step_static", "hs_destroy", "hs_last_error")
+HS_STATIC_PLAN_BYTES = 8 << 20
 
 
 class HiSparseError(RuntimeError):
@@ -77,6 +78,7 @@ def lib():
         L.hs_resolve.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         L.hs_plan.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp]
         L.hs_copy.argtypes = [vp, vp, vp, vp, vp]
+        L.hs_step_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
         L.hs_trial.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.hs_commit.argtypes = [vp, vp, vp, vp, vp, vp]
         L.hs_offload.argtypes = [vp, vp, vp, i32, vp, vp]
@@ -89,7 +91,7 @@ def lib():
         L.hs_last_error.restype = ctypes.c_char_p
         for name in ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
                      "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_offload", "hs_advance_tail", "hs_gather",
-                     "hs_rebuild_order"):
+                     "hs_rebuild_order", "hs_step_static"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -193,6 +195,12 @@ def hs_plan(ctx, topk, tail0, out, miss, status, plan, stream=None, row_sources:
 
 def hs_copy(ctx, plan, miss, gather=None, stream=None) -> None:
     _check(lib().hs_copy(ctx, _ptr(plan), _ptr(miss), _ptr(gather), _stream(stream)))
+
+
+def hs_step_static(ctx, topk, tail0, out, miss, status, gather=None, stream=None) -> None:
+    """hs_plan + hs_copy in one call with the plan in the library's static device array (allocates nothing)."""
+    _check(lib().hs_step_static(ctx, _ptr(topk), _ptr(tail0), _ptr(out), _ptr(miss), _ptr(status), _ptr(gather),
+                                _stream(stream)))
 
 
 def hs_trial(ctx, topk, tail0, out, miss, status, gather, trial, stream=None) -> None:

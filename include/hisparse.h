@@ -211,6 +211,20 @@ int hs_plan(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t*
 int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* d_gather, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation): the split step, hs_plan then hs_copy (with HS_PLAN_ROW_SOURCES when d_gather is
+ * given), in one call whose plan lives in the library's own static device array instead of a caller's plan
+ * buffer. Arguments and results are those of hs_resolve (d_gather nullable). The array holds HS_STATIC_PLAN_BYTES
+ * per device, kept until the process ends and shared by every call on that device: a context whose plan
+ * (R x 4 x top_k int32) is larger is refused with HS_E_INVALID, and calls that overlap on one device (other
+ * streams, other threads, other contexts) race. The array keeps the last call's plan; nothing in it has to
+ * start at zero. Allocates nothing.
+ */
+#define HS_STATIC_PLAN_BYTES (8u << 20)
+int hs_step_static(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
+                   int32_t* d_status, void* d_gather, void* stream);
+
+/*
  * A retryable step, for speculative decoding: the vLLM page names a per-step resolver plan that can be
  * retried and shares the request's hot state ("vLLM GLM 5.3 最適化: Hybrid HiSparse オフローディング",
  * section vLLM エコシステムとの統合).
