@@ -116,6 +116,7 @@ void fill_sizes(const hs_config* cfg, int32_t H, const hs::Layout& L, hs_sizes* 
   s->lru_order_bytes = R * B * 2;
   s->page_bytes = R * (uint64_t)H * 4;
   s->step_bytes = R * 4;
+  s->epoch_bytes = R * 4;
   s->topk_bytes = R * k * 4;
   s->out_bytes = R * k * 4;
   s->gather_bytes = R * k * rb;
@@ -126,6 +127,12 @@ void fill_sizes(const hs_config* cfg, int32_t H, const hs::Layout& L, hs_sizes* 
   const hs::Layout lp = hs::launch_layout(kk, BB, (int)H, TT, false, hs::kLdsCap);
   const hs::Layout lg = hs::launch_layout(kk, BB, (int)H, TT, true, hs::kLdsCap);
   s->lds_bytes_rank = L.total;
+  uint64_t tables = 0, rows = 0;
+  for (const uint64_t b : {s->slot_tok_bytes, s->stamp_bytes, s->lru_order_bytes, s->page_bytes, s->step_bytes})
+    tables += (b + 255) & ~255ull;
+  for (const uint64_t b : {s->hot_bytes, s->tail_bytes}) rows += (b + 255) & ~255ull;
+  s->state_tables_bytes = tables;
+  s->state_rows_bytes = rows;
   s->lds_bytes_launch = lp.total;
   s->lds_bytes_launch_gather = lg.total;
   s->lds_bytes = std::max(lp.total, lg.total);
@@ -263,6 +270,7 @@ int hs_bind_device(hs_ctx* ctx, const hs_device_views* v) {
       {v->lru_order, v->lru_order_bytes, s.lru_order_bytes, "lru_order", 2},
       {v->page, v->page_bytes, s.page_bytes, "page", 4},
       {v->step, v->step_bytes, s.step_bytes, "step", 4},
+      {v->epoch, v->epoch_bytes, s.epoch_bytes, "epoch", 4},
   };
   for (const Need& n : needs) {
     if (!n.p) return fail(HS_E_INVALID, "device buffer '%s' is NULL", n.name);
@@ -322,6 +330,7 @@ int hs_reset(hs_ctx* ctx, const int32_t* d_request_ids, int32_t n, void* stream)
   a.order = ctx->views.lru_order;
   a.page = ctx->views.page;
   a.step = ctx->views.step;
+  a.epoch = ctx->views.epoch;
   hipError_t e = hs::launch_reset(a, blocks, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "reset launch");
   return ok();
@@ -375,6 +384,7 @@ int resolve_common(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, i
   a.plan = d_plan;
   a.plan_sources = (plan_flags & HS_PLAN_ROW_SOURCES) ? 1 : 0;
   a.trial = d_trial;
+  a.epoch = ctx->views.epoch;
   a.trial_words = hs::trial_words(a.k, a.B);
   if (d_trial && !aligned(d_trial, 16)) return fail(HS_E_INVALID, "trial buffer is not 16-byte aligned");
   hipError_t e = hs::launch_resolve(a, (hipStream_t)stream);
@@ -420,6 +430,7 @@ int hs_commit(hs_ctx* ctx, const int32_t* d_trial, const void* d_gather, const i
   a.trial_words = hs::trial_words(a.k, a.B);
   a.trial = d_trial;
   a.accept = d_accept;
+  a.epoch = ctx->views.epoch;
   a.gather = (const hs::v4u*)d_gather;
   a.status = d_status;
   a.hot = (hs::v4u*)ctx->views.hot;
@@ -522,6 +533,7 @@ int hs_offload(hs_ctx* ctx, const void* d_rows, const int32_t* d_pos, int32_t n,
   a.host = (hs::v4u*)ctx->pool_dev;
   a.hot = (hs::v4u*)ctx->views.hot;
   a.page = ctx->views.page;
+  a.epoch = ctx->views.epoch;
   hipError_t e = hs::launch_offload(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "offload launch");
   return ok();
@@ -545,6 +557,7 @@ int hs_advance_tail(hs_ctx* ctx, int32_t* d_tail0, const int32_t* d_n, int32_t* 
   a.host = (hs::v4u*)ctx->pool_dev;
   a.hot = (hs::v4u*)ctx->views.hot;
   a.page = ctx->views.page;
+  a.epoch = ctx->views.epoch;
   hipError_t e = hs::launch_advance_tail(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "advance-tail launch");
   return ok();
@@ -561,6 +574,81 @@ int hs_rebuild_order(hs_ctx* ctx, void* stream) {
   hipError_t e = hs::launch_rebuild_order(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "rebuild-order launch");
   return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// The sections of a state snapshot, in their order, each at a 256-byte aligned offset: what they hold on the
+// device, their size, and whether they are tables (HS_STATE_TABLES) or rows (HS_STATE_ROWS).
+struct Section { void* dev; uint64_t bytes; uint32_t kind; };
+
+int state_sections(hs_ctx* ctx, uint32_t what, Section* sec, int* n, uint64_t* total) {
+  if (what == 0 || (what & ~(uint32_t)(HS_STATE_TABLES | HS_STATE_ROWS)))
+    return fail(HS_E_INVALID, "what must be HS_STATE_TABLES, HS_STATE_ROWS or both (got 0x%x)", (unsigned)what);
+  hs_sizes s;
+  fill_sizes(&ctx->cfg, ctx->H, ctx->layout, &s);
+  const hs_device_views& v = ctx->views;
+  const Section all[] = {
+      {v.slot_tok, s.slot_tok_bytes, HS_STATE_TABLES}, {v.stamp, s.stamp_bytes, HS_STATE_TABLES},
+      {v.lru_order, s.lru_order_bytes, HS_STATE_TABLES}, {v.page, s.page_bytes, HS_STATE_TABLES},
+      {v.step, s.step_bytes, HS_STATE_TABLES}, {v.hot, s.hot_bytes, HS_STATE_ROWS},
+      {v.tail, s.tail_bytes, HS_STATE_ROWS},
+  };
+  *n = 0;
+  *total = 0;
+  for (const Section& x : all) {
+    if (!(x.kind & what)) continue;
+    sec[(*n)++] = x;
+    *total += (x.bytes + 255) & ~255ull;
+  }
+  return HS_OK;
+}
+
+int copy_state(hs_ctx* ctx, void* snap, uint64_t snap_bytes, uint32_t what, bool to_snapshot, void* stream) {
+  int rc = check_ready(ctx);
+  if (rc) return rc;
+  if (!snap) return fail(HS_E_INVALID, "snapshot buffer is NULL");
+  Section sec[7];
+  int n = 0;
+  uint64_t total = 0;
+  rc = state_sections(ctx, what, sec, &n, &total);
+  if (rc) return rc;
+  if (snap_bytes < total)
+    return fail(HS_E_INVALID, "snapshot buffer has %llu bytes, needs %llu", (unsigned long long)snap_bytes,
+                (unsigned long long)total);
+  if (!aligned(snap, 256)) return fail(HS_E_INVALID, "snapshot buffer is not 256-byte aligned");
+  rc = check_device_buffer(ctx, snap, "snapshot");
+  if (rc) return rc;
+  uint64_t off = 0;
+  for (int i = 0; i < n; ++i) {
+    if (sec[i].bytes) {
+      char* p = static_cast<char*>(snap) + off;
+      hipError_t e = to_snapshot
+                         ? hipMemcpyAsync(p, sec[i].dev, sec[i].bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream)
+                         : hipMemcpyAsync(sec[i].dev, p, sec[i].bytes, hipMemcpyDeviceToDevice, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync of a state section");
+    }
+    off += (sec[i].bytes + 255) & ~255ull;
+  }
+  if (!to_snapshot) {
+    hipError_t e = hs::launch_bump_epoch(ctx->views.epoch, ctx->cfg.num_requests, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "epoch launch");
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int hs_export_state(hs_ctx* ctx, void* d_dst, uint64_t dst_bytes, uint32_t what, void* stream) {
+  return copy_state(ctx, d_dst, dst_bytes, what, true, stream);
+}
+
+int hs_import_state(hs_ctx* ctx, const void* d_src, uint64_t src_bytes, uint32_t what, void* stream) {
+  return copy_state(ctx, const_cast<void*>(d_src), src_bytes, what, false, stream);
 }
 
 void hs_destroy(hs_ctx* ctx) {

@@ -143,6 +143,7 @@ struct ResolveArgs {
                     // B + tail row, -1 none, -2 - j the j-th miss)
   int32_t plan_sources;
   int32_t* trial;   // non-null: trial launch, [R][trial_words]
+  const int32_t* epoch;  // [R] change counters (a trial records its request's)
   int64_t trial_words;
 };
 
@@ -155,6 +156,7 @@ struct CommitArgs {
   int64_t trial_words;
   const int32_t* trial;
   const int32_t* accept;  // [R] or nullptr (all)
+  const int32_t* epoch;   // [R] change counters: a record made under another value is stale
   const v4u* gather;      // [R][k][row16]
   int32_t* status;        // [R] or nullptr
   v4u* hot;
@@ -185,6 +187,7 @@ struct OffloadArgs {
   v4u* host;           // device address of the pinned pool
   v4u* hot;
   const int32_t* page;
+  int32_t* epoch;      // [R] change counters, advanced
 };
 
 struct AdvanceTailArgs {
@@ -196,6 +199,7 @@ struct AdvanceTailArgs {
   v4u* host;
   v4u* hot;
   const int32_t* page;
+  int32_t* epoch;      // [R] change counters, advanced where the window moves
 };
 
 struct RebuildArgs {
@@ -212,6 +216,7 @@ struct ResetArgs {
   uint16_t* order;
   int32_t* page;
   int32_t* step;
+  int32_t* epoch;      // [R] change counters, advanced (nullptr: leave them)
 };
 
 // gather_kernel: threads per workgroup, 16-byte loads in flight per thread, and the chunks one workgroup
@@ -236,6 +241,7 @@ hipError_t static_plan_address(void** ptr);
 
 hipError_t launch_resolve(const ResolveArgs& a, hipStream_t s);
 hipError_t launch_reset(const ResetArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_bump_epoch(int32_t* epoch, int R, hipStream_t s);
 hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 hipError_t launch_copy(const CopyArgs& a, hipStream_t s);
 hipError_t launch_rebuild_order(const RebuildArgs& a, hipStream_t s);

@@ -152,7 +152,7 @@ __device__ __forceinline__ void copy_missed_rows(const v4u* hostr, v4u* hotr, co
 constexpr int kFused = 0, kPlan = 1, kTrial = 2;
 constexpr int kTrialHead = 4;
 
-// Trial record of one request (int32 words): [m, first tail position of the new order, step, 0], then
+// Trial record of one request (int32 words): [m, first tail position of the new order, step, epoch], then
 // k missed tokens, k victim slots, k evicted tokens (-1: slot was empty), k positions in the selection,
 // then the new LRU order as B uint16.
 __device__ __forceinline__ int32_t* trial_rec(const ResolveArgs& a, int r) { return a.trial + (size_t)r * a.trial_words; }
@@ -162,7 +162,7 @@ __device__ __forceinline__ void trial_header(const ResolveArgs& a, int r, int m,
   rec[0] = m;
   rec[1] = tail_start;
   rec[2] = step;
-  rec[3] = 0;
+  rec[3] = a.epoch[r];
 }
 
 // A request whose state tables hold impossible values: every output -1 (zero rows gathered), no miss, status
@@ -1147,7 +1147,21 @@ __global__ __launch_bounds__(1024) void reset_kernel(ResetArgs a) {
     a.order[rB + s] = (uint16_t)s;
   }
   for (int x = threadIdx.x; x < a.H; x += blockDim.x) a.page[rH + x] = -1;
-  if (threadIdx.x == 0) a.step[r] = 0;
+  if (threadIdx.x == 0) {
+    a.step[r] = 0;
+    a.epoch[r] += 1;  // a pending trial of this request is stale now
+  }
+}
+
+// Every request's change counter advances by one (after an imported state).
+__global__ __launch_bounds__(256) void bump_epoch_kernel(int32_t* epoch, int R) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < R) epoch[r] += 1;
+}
+
+hipError_t launch_bump_epoch(int32_t* epoch, int R, hipStream_t s) {
+  hipLaunchKernelGGL(bump_epoch_kernel, dim3((R + 255) / 256), dim3(256), 0, s, epoch, R);
+  return hipGetLastError();
 }
 
 // Workgroup (b, r) gathers rows [b*rows, b*rows + rows) of request r's selection into one contiguous
@@ -1282,8 +1296,9 @@ __global__ __launch_bounds__(kGatherThreads) void copy_gather_kernel(CopyArgs a)
 
 // Applies accepted trial records: the new LRU order, stamp t for the hit and victim slots (the new order's
 // tail), the victims' slot-table and page-table entries, the step counter, and each missed row copied from
-// the gather output (where the trial put it) into its victim slot. A record whose step no longer matches
-// the request's step counter is stale and is not applied.
+// the gather output (where the trial put it) into its victim slot. A record whose step or epoch no longer
+// matches the request's is stale and is not applied: another step, a reset, an offload, a tail advance or an
+// imported state came in between, and the rows it gathered may no longer be the host pool's.
 __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint8_t* used = smem;  // B flags: slot in the new order's tail
@@ -1298,7 +1313,7 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   const int k = a.k, B = a.B, H = a.H;
   const int32_t* rec = a.trial + (size_t)r * a.trial_words;
   const int m = rec[0], u0 = rec[1], t = rec[2];
-  if (t < 0 || a.step[r] != t || m < 0 || m > k || u0 < 0 || u0 > B) {
+  if (t < 0 || a.step[r] != t || a.epoch[r] != rec[3] || m < 0 || m > k || u0 < 0 || u0 > B) {
     if (a.status && tid == 0) a.status[r] = kStatusStale;
     return;
   }
@@ -1418,6 +1433,7 @@ __global__ __launch_bounds__(256) void offload_kernel(OffloadArgs a) {
     if (s >= 0 && s < a.B) hotr[(size_t)s * row16 + q] = v;
   }
   if (a.status && skipped) a.status[r] = kStatusBadId;  // same value from every thread that skipped
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.epoch[r] += 1;  // a pending trial of this request is stale now
 }
 
 hipError_t launch_offload(const OffloadArgs& a, hipStream_t s) {
@@ -1464,6 +1480,7 @@ __global__ __launch_bounds__(1024) void advance_tail_kernel(AdvanceTailArgs a) {
   if (tid == 0) {
     a.tail0[r] = t0 + n;
     if (a.status) a.status[r] = skipped ? kStatusBadId : 0;
+    if (n > 0) a.epoch[r] += 1;  // a pending trial of this request is stale now
   }
 }
 

@@ -20,10 +20,11 @@ HS_OK, HS_E_INVALID, HS_E_NOMEM, HS_E_HIP, HS_E_STATE = 0, -1, -2, -3, -4
 HS_STATUS_BAD_ID, HS_STATUS_DUP_ID, HS_STATUS_BAD_STATE, HS_STATUS_STALE = 1, 2, 4, 8
 HS_EVICT_LRU, HS_EVICT_FIFO = 0, 1
 HS_PLAN_ROW_SOURCES = 1
+HS_STATE_TABLES, HS_STATE_ROWS = 1, 2
 
 EXPORTED = ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
             "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_offload", "hs_advance_tail", "hs_gather",
-            "hs_rebuild_order", "hs_step_static", "hs_destroy", "hs_last_error")
+            "hs_rebuild_order", "hs_step_static", "hs_export_state", "hs_import_state", "hs_destroy", "hs_last_error")
 HS_STATIC_PLAN_BYTES = 8 << 20
 
 
@@ -40,7 +41,7 @@ class HsConfig(ctypes.Structure):
 
 
 class HsDeviceViews(ctypes.Structure):
-    _fields_ = [(n, t) for name in ("hot", "tail", "slot_tok", "stamp", "lru_order", "page", "step")
+    _fields_ = [(n, t) for name in ("hot", "tail", "slot_tok", "stamp", "lru_order", "page", "step", "epoch")
                 for n, t in ((name, ctypes.c_void_p), (name + "_bytes", ctypes.c_uint64))]
 
 
@@ -51,7 +52,9 @@ class HsSizes(ctypes.Structure):
                 ("topk_bytes", ctypes.c_uint64), ("out_bytes", ctypes.c_uint64), ("gather_bytes", ctypes.c_uint64),
                 ("plan_bytes", ctypes.c_uint64), ("trial_bytes", ctypes.c_uint64), ("lds_bytes", ctypes.c_uint32),
                 ("lds_bytes_launch", ctypes.c_uint32), ("lds_bytes_launch_gather", ctypes.c_uint32),
-                ("token_slot_table", ctypes.c_uint32), ("lds_bytes_rank", ctypes.c_uint32)]
+                ("token_slot_table", ctypes.c_uint32), ("lds_bytes_rank", ctypes.c_uint32),
+                ("epoch_bytes", ctypes.c_uint64), ("state_tables_bytes", ctypes.c_uint64),
+                ("state_rows_bytes", ctypes.c_uint64)]
 
 
 def library_path() -> str:
@@ -79,6 +82,8 @@ def lib():
         L.hs_plan.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, vp]
         L.hs_copy.argtypes = [vp, vp, vp, vp, vp]
         L.hs_step_static.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp]
+        L.hs_export_state.argtypes = [vp, vp, ctypes.c_uint64, ctypes.c_uint32, vp]
+        L.hs_import_state.argtypes = [vp, vp, ctypes.c_uint64, ctypes.c_uint32, vp]
         L.hs_trial.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp]
         L.hs_commit.argtypes = [vp, vp, vp, vp, vp, vp]
         L.hs_offload.argtypes = [vp, vp, vp, i32, vp, vp]
@@ -91,7 +96,7 @@ def lib():
         L.hs_last_error.restype = ctypes.c_char_p
         for name in ("hs_required_sizes", "hs_create", "hs_host_pool", "hs_bind_device", "hs_reset", "hs_resolve",
                      "hs_plan", "hs_copy", "hs_trial", "hs_commit", "hs_offload", "hs_advance_tail", "hs_gather",
-                     "hs_rebuild_order", "hs_step_static"):
+                     "hs_rebuild_order", "hs_step_static", "hs_export_state", "hs_import_state"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -131,9 +136,22 @@ def hs_required_sizes(cfg: HsConfig) -> HsSizes:
     return s
 
 
+# Sizes of every live context, by its address: the calls below check each tensor against them (dtype and
+# element count, from tensor metadata only) before a pointer reaches the library, whose C calls take raw
+# pointers and cannot.
+_CTX_SIZES: Dict[int, Tuple[HsConfig, HsSizes]] = {}
+
+
+def _ctx_key(ctx) -> int:
+    if ctx is None:
+        return 0
+    return int(ctx.value or 0) if isinstance(ctx, ctypes.c_void_p) else int(ctx)
+
+
 def hs_create(cfg: HsConfig) -> ctypes.c_void_p:
     ctx = ctypes.c_void_p()
     _check(lib().hs_create(ctypes.byref(cfg), ctypes.byref(ctx)))
+    _CTX_SIZES[_ctx_key(ctx)] = (cfg, hs_required_sizes(cfg))
     return ctx
 
 
@@ -141,6 +159,32 @@ def hs_host_pool(ctx) -> Tuple[int, int, int]:
     base, stride, rows = ctypes.c_void_p(), ctypes.c_uint64(), ctypes.c_int32()
     _check(lib().hs_host_pool(ctx, ctypes.byref(base), ctypes.byref(stride), ctypes.byref(rows)))
     return base.value, stride.value, rows.value
+
+
+def _arg(name: str, t, ctx, *, int32: bool = True, count=None, nbytes=None, nullable: bool = False):
+    """Checks one tensor argument from its metadata and returns it (None when absent). int32 index arrays must be
+    torch.int32; row buffers may have any dtype but must hold nbytes. count / nbytes are functions of the
+    context's (config, sizes); without a known context only the dtype is checked (the library then refuses the
+    context)."""
+    if t is None:
+        if nullable:
+            return None
+        raise ValueError(f"{name} must not be None")
+    import torch
+    if int32 and t.dtype != torch.int32:
+        raise ValueError(f"{name} must be a torch.int32 tensor, got {t.dtype}")
+    info = _CTX_SIZES.get(_ctx_key(ctx))
+    if info is not None:
+        if count is not None and t.numel() < count(*info):
+            raise ValueError(f"{name} has {t.numel()} elements, the context needs at least {count(*info)}")
+        have = t.numel() * t.element_size()
+        if nbytes is not None and have < nbytes(*info):
+            raise ValueError(f"{name} has {have} bytes, the context needs at least {nbytes(*info)}")
+    return t
+
+
+_R = lambda c, s: c.num_requests  # noqa: E731
+_RK = lambda c, s: c.num_requests * c.top_k  # noqa: E731
 
 
 def _ptr(t) -> Optional[int]:
@@ -159,10 +203,10 @@ def _bytes(t) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
 
-def hs_bind_device(ctx, hot, tail, slot_tok, stamp, lru_order, page, step) -> None:
+def hs_bind_device(ctx, hot, tail, slot_tok, stamp, lru_order, page, step, epoch) -> None:
     v = HsDeviceViews()
     for name, t in (("hot", hot), ("tail", tail), ("slot_tok", slot_tok), ("stamp", stamp),
-                    ("lru_order", lru_order), ("page", page), ("step", step)):
+                    ("lru_order", lru_order), ("page", page), ("step", step), ("epoch", epoch)):
         if t is not None and not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         setattr(v, name, None if t is None else t.data_ptr())  # the library checks these itself
@@ -177,54 +221,106 @@ def _stream(stream) -> Optional[int]:
     return stream if isinstance(stream, int) else stream.cuda_stream
 
 
+def _ptrs(*tensors):
+    """Device addresses of already checked tensor arguments (None stays None)."""
+    return [_ptr(t) for t in tensors]
+
+
 def hs_reset(ctx, request_ids=None, stream=None) -> None:
     n = -1 if request_ids is None else request_ids.numel()
-    _check(lib().hs_reset(ctx, _ptr(request_ids), n, _stream(stream)))
+    (ids,) = _ptrs(_arg("request_ids", request_ids, ctx, nullable=True))
+    _check(lib().hs_reset(ctx, ids, n, _stream(stream)))
+
+
+def _step_args(ctx, topk, tail0, out, miss, status, gather, gather_required=False):
+    return (_arg("topk", topk, ctx, count=_RK), _arg("tail0", tail0, ctx, count=_R, nullable=True),
+            _arg("out", out, ctx, count=_RK), _arg("miss", miss, ctx, count=_R), _arg("status", status, ctx, count=_R),
+            _arg("gather", gather, ctx, int32=False, nbytes=lambda c, s: s.gather_bytes,
+                 nullable=not gather_required))
+
+
+def _plan_arg(ctx, plan):
+    return _arg("plan", plan, ctx, count=lambda c, s: s.plan_bytes // 4)
 
 
 def hs_resolve(ctx, topk, tail0, out, miss, status, gather=None, stream=None) -> None:
-    _check(lib().hs_resolve(ctx, _ptr(topk), _ptr(tail0), _ptr(out), _ptr(miss), _ptr(status), _ptr(gather),
-                            _stream(stream)))
+    _check(lib().hs_resolve(ctx, *_ptrs(*_step_args(ctx, topk, tail0, out, miss, status, gather)), _stream(stream)))
 
 
 def hs_plan(ctx, topk, tail0, out, miss, status, plan, stream=None, row_sources: bool = False) -> None:
     """row_sources: also record each position's row source, which a gathering hs_copy of this plan needs."""
-    _check(lib().hs_plan(ctx, _ptr(topk), _ptr(tail0), _ptr(out), _ptr(miss), _ptr(status), _ptr(plan),
-                         HS_PLAN_ROW_SOURCES if row_sources else 0, _stream(stream)))
+    a = _ptrs(*_step_args(ctx, topk, tail0, out, miss, status, None)[:5], _plan_arg(ctx, plan))
+    _check(lib().hs_plan(ctx, *a, HS_PLAN_ROW_SOURCES if row_sources else 0, _stream(stream)))
 
 
 def hs_copy(ctx, plan, miss, gather=None, stream=None) -> None:
-    _check(lib().hs_copy(ctx, _ptr(plan), _ptr(miss), _ptr(gather), _stream(stream)))
+    a = _ptrs(_plan_arg(ctx, plan), _arg("miss", miss, ctx, count=_R),
+              _arg("gather", gather, ctx, int32=False, nbytes=lambda c, s: s.gather_bytes, nullable=True))
+    _check(lib().hs_copy(ctx, *a, _stream(stream)))
 
 
 def hs_step_static(ctx, topk, tail0, out, miss, status, gather=None, stream=None) -> None:
     """hs_plan + hs_copy in one call with the plan in the library's static device array (allocates nothing)."""
-    _check(lib().hs_step_static(ctx, _ptr(topk), _ptr(tail0), _ptr(out), _ptr(miss), _ptr(status), _ptr(gather),
+    _check(lib().hs_step_static(ctx, *_ptrs(*_step_args(ctx, topk, tail0, out, miss, status, gather)),
                                 _stream(stream)))
 
 
+def _trial_arg(ctx, trial):
+    return _arg("trial", trial, ctx, nbytes=lambda c, s: s.trial_bytes)
+
+
 def hs_trial(ctx, topk, tail0, out, miss, status, gather, trial, stream=None) -> None:
-    _check(lib().hs_trial(ctx, _ptr(topk), _ptr(tail0), _ptr(out), _ptr(miss), _ptr(status), _ptr(gather),
-                          _ptr(trial), _stream(stream)))
+    a = _ptrs(*_step_args(ctx, topk, tail0, out, miss, status, gather, gather_required=True), _trial_arg(ctx, trial))
+    _check(lib().hs_trial(ctx, *a, _stream(stream)))
 
 
 def hs_commit(ctx, trial, gather, accept=None, status=None, stream=None) -> None:
-    _check(lib().hs_commit(ctx, _ptr(trial), _ptr(gather), _ptr(accept), _ptr(status), _stream(stream)))
+    a = _ptrs(_trial_arg(ctx, trial), _arg("gather", gather, ctx, int32=False, nbytes=lambda c, s: s.gather_bytes),
+              _arg("accept", accept, ctx, count=_R, nullable=True), _arg("status", status, ctx, count=_R, nullable=True))
+    _check(lib().hs_commit(ctx, *a, _stream(stream)))
 
 
 def hs_offload(ctx, rows, pos, status=None, stream=None) -> None:
-    """rows: device uint8 [R, n, row_bytes]; pos: device int32 [R]."""
-    _check(lib().hs_offload(ctx, _ptr(rows), _ptr(pos), int(rows.shape[1]) if rows is not None else 0,
-                            _ptr(status), _stream(stream)))
+    """rows: device [R, n, row_bytes] (uint8, or any dtype whose last dimension spans row_bytes); pos: device
+    int32 [R]."""
+    if rows is None:
+        raise ValueError("rows must not be None")
+    info = _CTX_SIZES.get(_ctx_key(ctx))
+    if rows.dim() != 3:
+        raise ValueError(f"rows must be [requests, n, row] (3 dimensions), got shape {tuple(rows.shape)}")
+    if info is not None:
+        cfg = info[0]
+        if rows.shape[0] != cfg.num_requests or rows.shape[2] * rows.element_size() != cfg.row_bytes:
+            raise ValueError(f"rows must be [{cfg.num_requests}, n, {cfg.row_bytes} bytes], got shape "
+                             f"{tuple(rows.shape)} of {rows.dtype}")
+    a = _ptrs(_arg("rows", rows, ctx, int32=False), _arg("pos", pos, ctx, count=_R),
+              _arg("status", status, ctx, count=_R, nullable=True))
+    _check(lib().hs_offload(ctx, a[0], a[1], int(rows.shape[1]), a[2], _stream(stream)))
 
 
 def hs_advance_tail(ctx, tail0, n, status=None, stream=None) -> None:
     """tail0: device int32 [R], advanced in place; n: device int32 [R]."""
-    _check(lib().hs_advance_tail(ctx, _ptr(tail0), _ptr(n), _ptr(status), _stream(stream)))
+    a = _ptrs(_arg("tail0", tail0, ctx, count=_R), _arg("n", n, ctx, count=_R),
+              _arg("status", status, ctx, count=_R, nullable=True))
+    _check(lib().hs_advance_tail(ctx, *a, _stream(stream)))
 
 
 def hs_gather(ctx, out, gather, stream=None) -> None:
-    _check(lib().hs_gather(ctx, _ptr(out), _ptr(gather), _stream(stream)))
+    a = _ptrs(_arg("out", out, ctx, count=_RK),
+              _arg("gather", gather, ctx, int32=False, nbytes=lambda c, s: s.gather_bytes))
+    _check(lib().hs_gather(ctx, *a, _stream(stream)))
+
+
+def hs_export_state(ctx, dst, what: int = 3, stream=None) -> None:
+    """dst: a device tensor of at least state_tables_bytes / state_rows_bytes (as what selects); the library
+    checks its byte size."""
+    (p,) = _ptrs(_arg("dst", dst, ctx, int32=False))
+    _check(lib().hs_export_state(ctx, p, _bytes(dst), what, _stream(stream)))
+
+
+def hs_import_state(ctx, src, what: int = 3, stream=None) -> None:
+    (p,) = _ptrs(_arg("src", src, ctx, int32=False))
+    _check(lib().hs_import_state(ctx, p, _bytes(src), what, _stream(stream)))
 
 
 def hs_rebuild_order(ctx, stream=None) -> None:
@@ -233,6 +329,7 @@ def hs_rebuild_order(ctx, stream=None) -> None:
 
 def hs_destroy(ctx) -> None:
     if ctx:
+        _CTX_SIZES.pop(_ctx_key(ctx), None)
         lib().hs_destroy(ctx)
 
 
@@ -258,7 +355,9 @@ class SwapIn:
         self.lru_order = torch.empty((self.R, self.B), dtype=torch.int16, device=dev)
         self.page = torch.empty((self.R, self.H), dtype=torch.int32, device=dev)
         self.step = torch.empty((self.R,), dtype=torch.int32, device=dev)
-        hs_bind_device(self.ctx, self.hot, self.tail, self.slot_tok, self.stamp, self.lru_order, self.page, self.step)
+        self.epoch = torch.zeros((self.R,), dtype=torch.int32, device=dev)
+        hs_bind_device(self.ctx, self.hot, self.tail, self.slot_tok, self.stamp, self.lru_order, self.page, self.step,
+                       self.epoch)
         hs_reset(self.ctx)
 
     def host_pool(self) -> np.ndarray:
@@ -288,6 +387,14 @@ class SwapIn:
     def trial_buffer(self):
         import torch
         return torch.empty((self.sizes.trial_bytes // 4,), dtype=torch.int32, device=self.device)
+
+    def state_buffer(self, what: int = 3):
+        """A device buffer for hs_export_state / hs_import_state of what (HS_STATE_TABLES | HS_STATE_ROWS), zeroed
+        so that the alignment padding between sections (never written) compares equal across snapshots."""
+        import torch
+        n = (self.sizes.state_tables_bytes if what & HS_STATE_TABLES else 0) + \
+            (self.sizes.state_rows_bytes if what & HS_STATE_ROWS else 0)
+        return torch.zeros((n,), dtype=torch.uint8, device=self.device)
 
     def plan_buffer(self):
         import torch

@@ -59,8 +59,8 @@ extern "C" {
 #define HS_STATUS_DUP_ID 2    /* an id repeated within the request's selection (first occurrence wins) */
 #define HS_STATUS_BAD_STATE 4 /* the request's slot table or LRU order held an impossible value: nothing
                                  was changed for this request and every output is -1 */
-#define HS_STATUS_STALE 8     /* hs_commit: the trial was planned at another step than the request's current
-                                 one; it was not applied */
+#define HS_STATUS_STALE 8     /* hs_commit: the request changed since the trial (another step, a reset, an
+                                 offload, a tail advance or an imported state); it was not applied */
 
 /*
  * Configuration. top_k, device_buffer_size and host_to_device_ratio are the
@@ -106,8 +106,9 @@ typedef struct hs_config {
  * Device buffers (caller-owned). Sizes are in bytes and must be at least what
  * hs_required_sizes reports; pointers must be 16-byte aligned (hot, tail,
  * gather output) or 4-byte aligned (tables). H = host rows per request.
- * The tables are written by the library; a caller that writes them (restoring
- * a snapshot, for instance) must leave a consistent state. Out-of-range
+ * The tables are written by the library; a caller that writes them itself
+ * (hs_import_state aside) must leave a consistent state, and must not then
+ * commit a trial made before the write. Out-of-range
  * entries are caught (HS_STATUS_BAD_STATE); a slot table holding one token in
  * two slots is not: a step that selects that token reports either slot.
  */
@@ -120,6 +121,10 @@ typedef struct hs_device_views {
   uint16_t* lru_order;  uint64_t lru_order_bytes; /* [R][B] slots in ascending (stamp, slot) (library-maintained) */
   int32_t* page;        uint64_t page_bytes;      /* [R][H] slot of each token, -1 = not in the hot buffer */
   int32_t* step;        uint64_t step_bytes;      /* [R] step counter of each request */
+  int32_t* epoch;       uint64_t epoch_bytes;     /* [R] change counter of each request (library-maintained, any
+                                                     initial contents): hs_reset, hs_offload, hs_advance_tail and
+                                                     hs_import_state advance it; hs_commit refuses a trial made
+                                                     under another value */
 } hs_device_views;
 
 typedef struct hs_sizes {
@@ -138,6 +143,9 @@ typedef struct hs_sizes {
   uint32_t token_slot_table;        /* bit 0: launches without a gather output use the direct layout;
                                        bit 1: launches with one do */
   uint32_t lds_bytes_rank;          /* LDS of the rank layout of this shape (whether or not launches take it) */
+  uint64_t epoch_bytes;             /* [R] int32 change counters */
+  uint64_t state_tables_bytes;      /* snapshot of the tables (HS_STATE_TABLES), see hs_export_state */
+  uint64_t state_rows_bytes;        /* snapshot of the hot and tail rows (HS_STATE_ROWS) */
 } hs_sizes;
 
 typedef struct hs_ctx hs_ctx;
@@ -274,9 +282,28 @@ int hs_advance_tail(hs_ctx* ctx, int32_t* d_tail0, const int32_t* d_n, int32_t* 
  * an index outside [0, B + T). d_out [R][k] int32, d_gather [R][k][row_bytes]. */
 int hs_gather(hs_ctx* ctx, const int32_t* d_out, void* d_gather, void* stream);
 
-/* Rebuild every request's LRU order list from its stamps (ascending (stamp, slot)). Call it after
- * writing slot_tok / stamp / page / step from a snapshot that did not carry lru_order; a snapshot of all
- * seven device buffers restores without it. */
+/*
+ * Snapshots of a context's device state, for tests, benchmarks and the retryable step ("vLLM GLM 5.3 最適化:
+ * Hybrid HiSparse オフローディング", section vLLM エコシステムとの統合: a per-step resolver plan that shares the
+ * request's hot state and can be retried).
+ * what selects HS_STATE_TABLES (slot table, stamps, LRU order list, page table, step counters), HS_STATE_ROWS
+ * (hot rows and device tail rows) or both. The snapshot (device memory of the context's device, 256-byte
+ * aligned, at least hs_sizes.state_tables_bytes and/or .state_rows_bytes) holds the selected buffers in the
+ * order slot_tok, stamp, lru_order, page, step, hot, tail, each at the next 256-byte aligned offset, byte for
+ * byte as the bound buffers hold them. Both calls are stream-ordered device-to-device copies and allocate
+ * nothing. hs_import_state writes the snapshot back (it must come from a context of the same configuration,
+ * with the same what) and then advances every request's change counter, so no trial made before the import
+ * can be committed after it. HS_E_INVALID for a bad what, a small or misaligned buffer, or one that is not
+ * device memory of the context's device.
+ */
+#define HS_STATE_TABLES 1u
+#define HS_STATE_ROWS 2u
+int hs_export_state(hs_ctx* ctx, void* d_dst, uint64_t dst_bytes, uint32_t what, void* stream);
+int hs_import_state(hs_ctx* ctx, const void* d_src, uint64_t src_bytes, uint32_t what, void* stream);
+
+/* Rebuild every request's LRU order list from its stamps (ascending (stamp, slot)). Call it after a caller
+ * writes slot_tok / stamp / page / step itself without the order list (hs_import_state restores the order list
+ * with the rest). */
 int hs_rebuild_order(hs_ctx* ctx, void* stream);
 
 /* Free the host pool and the context (device buffers belong to the caller). NULL is ignored. */

@@ -2,7 +2,8 @@
 // Python and no torch. It runs a few resolve steps and checks, on what the device returns, the properties every
 // step must have: each selected id resolves to a slot that holds it, the page table is the slot table's
 // inverse, the gathered row is the id's host row, and the miss count is the number of ids that were not
-// resident before the step. Exit status 0 when every check holds.
+// resident before the step. Then a snapshot through hs_export_state: the steps after it, replayed from the
+// imported snapshot, give the same outputs and the same state. Exit status 0 when every check holds.
 #include <hip/hip_runtime.h>
 
 #include <cstdio>
@@ -63,12 +64,14 @@ int main() {
   HIP(hipMalloc((void**)&v.lru_order, sz.lru_order_bytes));
   HIP(hipMalloc((void**)&v.page, sz.page_bytes));
   HIP(hipMalloc((void**)&v.step, sz.step_bytes));
+  HIP(hipMalloc((void**)&v.epoch, sz.epoch_bytes));
   v.hot_bytes = sz.hot_bytes;
   v.slot_tok_bytes = sz.slot_tok_bytes;
   v.stamp_bytes = sz.stamp_bytes;
   v.lru_order_bytes = sz.lru_order_bytes;
   v.page_bytes = sz.page_bytes;
   v.step_bytes = sz.step_bytes;
+  v.epoch_bytes = sz.epoch_bytes;
   HS(hs_bind_device(ctx, &v));
   HS(hs_reset(ctx, nullptr, -1, nullptr));
 
@@ -83,7 +86,14 @@ int main() {
   std::vector<int32_t> topk((size_t)R * k), out((size_t)R * k), miss(R), status(R), slot_tok((size_t)R * B),
       page((size_t)R * H), prev_slot_tok((size_t)R * B, -1);
   std::vector<uint8_t> gather(sz.gather_bytes);
+  const uint64_t snap_bytes = sz.state_tables_bytes + sz.state_rows_bytes;
+  void* d_snap = nullptr;
+  HIP(hipMalloc(&d_snap, snap_bytes));
+  const int snap_step = steps / 2;
+  std::vector<std::vector<int32_t>> outs_after;  // outputs of the steps after the snapshot
+  std::vector<uint8_t> state_end, state_replay;
   for (int t = 0; t < steps; ++t) {
+    if (t == snap_step) HS(hs_export_state(ctx, d_snap, snap_bytes, HS_STATE_TABLES | HS_STATE_ROWS, nullptr));
     // a sliding window of distinct ids per request
     for (int r = 0; r < R; ++r) {
       const int base = (t * 23 + r * 101) % H;
@@ -122,19 +132,46 @@ int main() {
       EXPECT(mapped == occupied, "step %d request %d: %d page entries for %d occupied slots", t, r, mapped, occupied);
     }
     prev_slot_tok = slot_tok;
+    if (t >= snap_step) outs_after.push_back(out);
   }
+  // the state after the last step, then the same steps again from the imported snapshot
+  state_end.resize(snap_bytes);
+  state_replay.resize(snap_bytes);
+  void* d_end = nullptr;
+  HIP(hipMalloc(&d_end, snap_bytes));
+  HS(hs_export_state(ctx, d_end, snap_bytes, HS_STATE_TABLES | HS_STATE_ROWS, nullptr));
+  HIP(hipDeviceSynchronize());
+  HIP(hipMemcpy(state_end.data(), d_end, snap_bytes, hipMemcpyDeviceToHost));
+  HS(hs_import_state(ctx, d_snap, snap_bytes, HS_STATE_TABLES | HS_STATE_ROWS, nullptr));
+  for (int t = snap_step; t < steps; ++t) {
+    for (int r = 0; r < R; ++r) {
+      const int base = (t * 23 + r * 101) % H;
+      for (int i = 0; i < k; ++i) topk[(size_t)r * k + i] = (base + i * 3) % H;
+    }
+    HIP(hipMemcpy(d_topk, topk.data(), sz.topk_bytes, hipMemcpyHostToDevice));
+    HS(hs_resolve(ctx, d_topk, nullptr, d_out, d_miss, d_status, d_gather, nullptr));
+    HIP(hipMemcpy(out.data(), d_out, sz.out_bytes, hipMemcpyDeviceToHost));
+    EXPECT(out == outs_after[(size_t)(t - snap_step)], "replayed step %d: outputs differ after the import", t);
+  }
+  HS(hs_export_state(ctx, d_end, snap_bytes, HS_STATE_TABLES | HS_STATE_ROWS, nullptr));
+  HIP(hipDeviceSynchronize());
+  HIP(hipMemcpy(state_replay.data(), d_end, snap_bytes, hipMemcpyDeviceToHost));
+  EXPECT(state_end == state_replay, "the replayed state differs from the state of the first run");
+  HIP(hipFree(d_end));
+  HIP(hipFree(d_snap));
   HIP(hipFree(d_gather));
   HIP(hipFree(d_status));
   HIP(hipFree(d_miss));
   HIP(hipFree(d_out));
   HIP(hipFree(d_topk));
   HIP(hipFree(v.step));
+  HIP(hipFree(v.epoch));
   HIP(hipFree(v.page));
   HIP(hipFree(v.lru_order));
   HIP(hipFree(v.stamp));
   HIP(hipFree(v.slot_tok));
   HIP(hipFree(v.hot));
   hs_destroy(ctx);
-  std::printf("c client: %d steps x %d requests consistent through the C ABI\n", steps, R);
+  std::printf("c client: %d steps x %d requests consistent through the C ABI, snapshot replay identical\n", steps, R);
   return 0;
 }

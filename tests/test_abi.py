@@ -180,3 +180,76 @@ def test_token_slot_table_where_it_fits():
             else:
                 assert got == s.lds_bytes_rank, (k, B, H, bit, got, s.lds_bytes_rank)
         assert s.lds_bytes == max(s.lds_bytes_launch, s.lds_bytes_launch_gather)
+
+
+@pytest.fixture()
+def fake_ctx():
+    """A context key registered with the sizes of a real configuration (host-only), so the binding's argument
+    checks run; no call below gets past them to the library."""
+    cfg = hm.config(3, 8, 16, 0.0, 64, 100, 4)
+    key = 0x5EED0000
+    hm.hisparse._CTX_SIZES[key] = (cfg, hm.hs_required_sizes(cfg))
+    yield ctypes.c_void_p(key)
+    hm.hisparse._CTX_SIZES.pop(key, None)
+
+
+def _i32(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.int32)
+
+
+def test_binding_checks_dtype_and_size(fake_ctx):
+    """Every per-call tensor is checked for dtype and size against the context before its pointer is taken: an
+    int64 id list, a short output, a gather output of too few bytes, a 2-D offload row block are refused with a
+    message that names the argument; a well-formed CPU tensor gets as far as the device check."""
+    import torch
+    ctx = fake_ctx
+    R, k, rb = 3, 8, 64
+    good = dict(topk=_i32(R, k), tail0=_i32(R), out=_i32(R, k), miss=_i32(R), status=_i32(R))
+    cases = [
+        (hm.hs_resolve, dict(good, topk=torch.zeros((R, k), dtype=torch.int64)), "topk must be a torch.int32"),
+        (hm.hs_resolve, dict(good, out=_i32(R, k - 1)), "out has 21 elements"),
+        (hm.hs_resolve, dict(good, miss=_i32(R - 1)), "miss has 2 elements"),
+        (hm.hs_resolve, dict(good, tail0=torch.zeros(R, dtype=torch.int64)), "tail0 must be a torch.int32"),
+        (hm.hs_resolve, dict(good, gather=torch.zeros((R, k, rb - 1), dtype=torch.uint8)), "gather has"),
+        (hm.hs_plan, dict(good, plan=_i32(R, 3, k)), "plan has 72 elements"),
+        (hm.hs_trial, dict(good, gather=torch.zeros((R, k, rb), dtype=torch.uint8), trial=_i32(4)), "trial has"),
+        (hm.hs_trial, dict(good, gather=None, trial=_i32(1 << 16)), "gather must not be None"),
+        (hm.hs_step_static, dict(good, status=torch.zeros(R, dtype=torch.float32)), "status must be a torch.int32"),
+    ]
+    for fn, kw, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            fn(ctx, **kw)
+    with pytest.raises(ValueError, match="plan has"):
+        hm.hs_copy(ctx, _i32(R, 2, k), _i32(R))
+    with pytest.raises(ValueError, match="gather has"):
+        hm.hs_gather(ctx, _i32(R, k), torch.zeros(10, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="accept has"):
+        hm.hs_commit(ctx, _i32(1 << 16), torch.zeros((R, k, rb), dtype=torch.uint8), accept=_i32(1))
+    with pytest.raises(ValueError, match="3 dimensions"):
+        hm.hs_offload(ctx, torch.zeros((R, 2 * rb), dtype=torch.uint8), _i32(R))
+    with pytest.raises(ValueError, match="rows must be"):
+        hm.hs_offload(ctx, torch.zeros((R, 2, rb // 2), dtype=torch.uint8), _i32(R))
+    with pytest.raises(ValueError, match="n must be a torch.int32"):
+        hm.hs_advance_tail(ctx, _i32(R), torch.zeros(R, dtype=torch.int64))
+    with pytest.raises(ValueError, match="request_ids must be a torch.int32"):
+        hm.hs_reset(ctx, torch.zeros(2, dtype=torch.int64))
+    # well-formed arguments on the CPU: refused only because they are not GPU tensors
+    with pytest.raises(ValueError, match="GPU tensor"):
+        hm.hs_resolve(ctx, **good)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        hm.hs_offload(ctx, torch.zeros((R, 2, rb), dtype=torch.uint8), _i32(R))
+
+
+def test_state_snapshot_sizes():
+    """hs_export_state / hs_import_state lay the selected buffers out at 256-byte aligned offsets: tables (slot
+    table, stamps, order list, page table, step counters) and rows (hot, tail)."""
+    cfg = hm.config(3, 8, 16, 0.0, 64, 100, 4)
+    s = hm.hs_required_sizes(cfg)
+    a256 = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert s.state_tables_bytes == sum(a256(b) for b in (3 * 16 * 4, 3 * 16 * 4, 3 * 16 * 2, 3 * 100 * 4, 3 * 4))
+    assert s.state_rows_bytes == a256(3 * 16 * 64) + a256(3 * 4 * 64)
+    assert s.epoch_bytes == 3 * 4
+    lib = hm.lib()
+    assert lib.hs_export_state(None, None, 0, 1, None) == hm.HS_E_INVALID
+    assert lib.hs_import_state(None, None, 0, 1, None) == hm.HS_E_INVALID

@@ -389,7 +389,8 @@ def test_bind_rejects_host_memory():
                    stamp=torch.empty((2, 16), dtype=torch.int32, device="cuda"),
                    lru_order=torch.empty((2, 16), dtype=torch.int16, device="cuda"),
                    page=torch.empty((2, 32), dtype=torch.int32, device="cuda"),
-                   step=torch.empty((2,), dtype=torch.int32, device="cuda"))
+                   step=torch.empty((2,), dtype=torch.int32, device="cuda"),
+                   epoch=torch.empty((2,), dtype=torch.int32, device="cuda"))
         for host in (torch.empty((2, 32), dtype=torch.int32),
                      torch.empty((2, 32), dtype=torch.int32, pin_memory=True)):
             with pytest.raises(hm.HiSparseError) as err:
@@ -645,6 +646,96 @@ def test_snapshot_restore_resume():
     for i in range(10, 20):
         p.step()
         assert (p.outs[0].cpu().numpy() == first[i - 10]).all()
+    p.check_state()
+    p.close()
+
+
+def test_export_import_state_replays_exactly():
+    """hs_export_state / hs_import_state: a snapshot of tables and rows taken after 10 steps, imported after 10
+    more, replays those 10 steps with the same outputs and ends in the same state; a tables-only import leaves
+    the hot rows as they are; the oracle agrees with the replay."""
+    import hierarchical_memory_amd as hm
+    w = workload.GROW_32.with_(num_requests=4, steps=24)
+    p = Pair(w, gather=True)
+    for _ in range(10):
+        p.step()
+    snap = p.sw.state_buffer(hm.HS_STATE_TABLES | hm.HS_STATE_ROWS)
+    hm.hs_export_state(p.sw.ctx, snap)
+    o_snap = {n: getattr(p.o, n).copy() for n in ("hot", "slot_tok", "stamp", "page", "t")}
+    first = []
+    for _ in range(10, 20):
+        p.step()
+        first.append((p.outs[0].cpu().numpy().copy(), p.outs[3].cpu().numpy().copy()))
+    end = p.sw.state_buffer()
+    hm.hs_export_state(p.sw.ctx, end)
+    hm.hs_import_state(p.sw.ctx, snap)
+    for n, v in o_snap.items():
+        getattr(p.o, n)[...] = v
+    p.t = 10
+    p.check_state()
+    for i in range(10, 20):
+        p.step()
+        assert (p.outs[0].cpu().numpy() == first[i - 10][0]).all() and (p.outs[3].cpu().numpy() == first[i - 10][1]).all()
+    again = p.sw.state_buffer()
+    hm.hs_export_state(p.sw.ctx, again)
+    assert torch.equal(end, again)
+    # tables only: the rows stay as they are
+    tables = p.sw.state_buffer(hm.HS_STATE_TABLES)
+    hm.hs_export_state(p.sw.ctx, tables, hm.HS_STATE_TABLES)
+    hot = p.sw.hot.clone()
+    p.sw.hot.fill_(3)
+    hm.hs_import_state(p.sw.ctx, tables, hm.HS_STATE_TABLES)
+    assert (p.sw.hot == 3).all()
+    p.sw.hot.copy_(hot)
+    p.check_state()
+    # a buffer too small, or a what of nothing, is refused before any copy
+    with pytest.raises(hm.HiSparseError) as err:
+        hm.hs_export_state(p.sw.ctx, tables, hm.HS_STATE_TABLES | hm.HS_STATE_ROWS)
+    assert err.value.code == hm.HS_E_INVALID
+    with pytest.raises(hm.HiSparseError):
+        hm.hs_import_state(p.sw.ctx, tables, 0)
+    p.close()
+
+
+def test_commit_after_an_offload_or_reset_is_stale():
+    """A trial, then an offload of the rows it fetched (the host pool now holds other rows), then the commit:
+    the commit is refused (HS_STATUS_STALE) and leaves the state as the offload left it, so no slot ends up with
+    a row the host pool no longer holds; a new trial and commit then serve the offloaded rows. Likewise a trial
+    made before a reset cannot be committed after the same number of steps has brought the step counter back."""
+    import hierarchical_memory_amd as hm
+    w = workload.GROW_32.with_(num_requests=4, steps=12)
+    p = Pair(w, gather=True)
+    R, rb = w.num_requests, w.row_bytes
+    trial = p.sw.trial_buffer()
+    out, miss, status, g = p.outs
+    cstat = torch.zeros((R,), dtype=torch.int32, device="cuda")
+    for _ in range(4):
+        p.step()
+    ids = np.ascontiguousarray(p.ids[:, 4])
+    topk = torch.from_numpy(ids).cuda()
+    hm.hs_trial(p.sw.ctx, topk, None, out, miss, status, g, trial)
+    torch.cuda.synchronize()
+    # offload 8 rows per request over the first missed tokens of the trial: the host pool changes under them
+    rec = trial.view(R, -1).cpu().numpy()
+    pos = rec[:, 4].astype(np.int32).copy()  # each request's smallest missed token
+    rows = np.random.default_rng(3).integers(0, 256, size=(R, 8, rb), dtype=np.uint8)
+    hm.hs_offload(p.sw.ctx, torch.from_numpy(rows).cuda(), torch.from_numpy(pos).cuda())
+    p.o.offload(rows, pos)
+    hm.hs_commit(p.sw.ctx, trial, g, None, cstat)
+    assert (cstat.cpu().numpy() == hm.HS_STATUS_STALE).all()
+    p.check_state()  # the oracle had the offload, not the trial
+    p.step(check_state=True)  # the same selection again: the missed rows come from the new host rows
+    # reset, the same number of steps again, then an old trial: stale
+    hm.hs_trial(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(p.ids[:, 5])).cuda(), None, out, miss, status, g, trial)
+    step_before = int(p.sw.step[0].item())
+    p.sw.reset()
+    p.o.reset()
+    for t in range(step_before):
+        p.o.step(p.ids[:, t])
+        hm.hs_resolve(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(p.ids[:, t])).cuda(), None, out, miss, status, g)
+    assert int(p.sw.step[0].item()) == step_before
+    hm.hs_commit(p.sw.ctx, trial, g, None, cstat)
+    assert (cstat.cpu().numpy() == hm.HS_STATUS_STALE).all()
     p.check_state()
     p.close()
 

@@ -1,7 +1,7 @@
 """GPU parity over random sequences of calls: every entry point of the C ABI interleaved on one context.
 
 Each sequence mixes fused resolves (with and without the gather), plan + copy (with and without the gather),
-accepted and rejected trials,
+the static-plan step, accepted and rejected trials, trials made stale by an offload before their commit,
 offloads, tail advances, partial resets and unfused gathers, in a seeded random order, on a small shape with a
 device tail. After every call its outputs and the whole device state (tables, stamps, step counters, hot rows,
 tail rows, tail starts, the host pool) must equal the oracle's, bit for bit.
@@ -30,7 +30,7 @@ import workload  # noqa: E402
 from tests.parity import Pair, log  # noqa: E402
 
 OPS = ("resolve", "resolve_gather", "plan_copy", "plan_copy_gather", "trial_accept", "trial_reject", "offload",
-       "advance_tail", "reset_some", "gather")
+       "advance_tail", "reset_some", "gather", "trial_offload_commit", "static_step")
 
 
 def _ids(rng, R, k, H):
@@ -90,9 +90,29 @@ def test_random_call_sequences(seed):
             op = "resolve"
         ids = _ids(rng, R, k, H)
         topk = torch.from_numpy(ids).cuda()
-        if op in ("resolve", "resolve_gather", "plan_copy", "plan_copy_gather", "trial_accept", "trial_reject"):
+        if op == "trial_offload_commit":
+            # a trial, an offload in between, then the commit: stale for every request (the offload changed each
+            # one), so the state is the offload's alone
+            hm.hs_trial(ctx, topk, p.tail0_dev, out, miss, status, g, trial)
+            o_out, o_miss, o_st, o_g = _clone(o).step(ids, p.tail0, gather=True)
+            _eq(out, o_out, "trial out", op, n)
+            _eq(g, o_g, "trial rows", op, n)
+            m_rows = int(rng.integers(1, 6))
+            pos = rng.integers(0, H - m_rows, size=R).astype(np.int32)
+            rows = rng.integers(0, 256, size=(R, m_rows, rb), dtype=np.uint8)
+            hm.hs_offload(ctx, torch.from_numpy(rows).cuda(), torch.from_numpy(pos).cuda())
+            o.offload(rows, pos)
+            st.zero_()
+            hm.hs_commit(ctx, trial, g, None, st)
+            _eq(st, np.full(R, hm.HS_STATUS_STALE, np.int32), "commit status", op, n)
+            resolved = True
+        elif op in ("resolve", "resolve_gather", "plan_copy", "plan_copy_gather", "trial_accept", "trial_reject",
+                    "static_step"):
             gather = op in ("resolve_gather", "plan_copy_gather", "trial_accept", "trial_reject")
-            if op in ("resolve", "resolve_gather"):
+            if op == "static_step":
+                gather = bool(rng.integers(0, 2))
+                hm.hs_step_static(ctx, topk, p.tail0_dev, out, miss, status, g if gather else None)
+            elif op in ("resolve", "resolve_gather"):
                 hm.hs_resolve(ctx, topk, p.tail0_dev, out, miss, status, g if gather else None)
             elif op in ("plan_copy", "plan_copy_gather"):
                 hm.hs_plan(ctx, topk, p.tail0_dev, out, miss, status, plan, row_sources=gather)
