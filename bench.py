@@ -5,7 +5,12 @@ A step is one hs_resolve over every request of the workload (one decode step): h
 table update and the copy of every missed row from pinned host memory into HBM. Inputs (the per-step top-k
 ids) are staged in HBM before the timed region. The JSON line reports resolved top-k entries/s (the value),
 the miss-copy rate against the host link, HBM figures, the roofline of the resolve kernel and the CPU oracle
-timed on a bounded sample of the same workload.
+timed on a bounded sample of the same workload. Further legs, each from a reset on the same stream: the split
+step (hs_plan + hs_copy) and the plans alone back to back (the hit path, priced against HBM), the split step
+pipelined over two streams, the copy beside independent HBM-bound work, a captured graph, the unfused gather,
+the retryable step, and the residency transitions (offload, tail advance). Measured traffic, where given, comes
+from a committed rocprofv3 summary of the same sources and workload, beside the algorithmic bytes it is
+compared with.
 """
 from __future__ import annotations
 
@@ -32,10 +37,13 @@ def kernel_source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+TRAFFIC_SOURCE = "profiles/pmc_traffic.json (rocprofv3 --pmc FETCH_SIZE, WRITE_SIZE of an earlier run on these sources)"
+
+
 def measured_traffic(workload_name: str, kernel: str):
-    """HBM+link bytes per launch from the committed rocprofv3 --pmc summary (FETCH_SIZE, WRITE_SIZE, each
-    scaled by what the same counter reads for a 1 GiB device copy), or None when that summary was taken on
-    other kernel sources or another workload."""
+    """Bytes per launch (reads + writes, HBM and host link together) from the committed rocprofv3 --pmc summary
+    (FETCH_SIZE, WRITE_SIZE, each scaled by what the same counter reads for a 1 GiB device copy), or None when
+    that summary was taken on other kernel sources or another workload. Not measured in this run."""
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     if not os.path.exists(path):
         return None
@@ -45,6 +53,15 @@ def measured_traffic(workload_name: str, kernel: str):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k["fetch_bytes"] + k["write_bytes"]
+
+
+def traffic_fields(workload_name: str, kernel: str, algorithmic_total: float) -> dict:
+    """The measured traffic beside the algorithmic bytes it is to be compared with: both count reads and writes,
+    HBM and host link together."""
+    t = measured_traffic(workload_name, kernel)
+    return {"traffic": t, "algorithmic_total_bytes": algorithmic_total,
+            "traffic_ratio": (t / algorithmic_total) if t and algorithmic_total else None,
+            "traffic_source": TRAFFIC_SOURCE if t else None}
 
 
 def log(msg: str) -> None:
@@ -142,10 +159,27 @@ def copy_probes(hm, torch, np, sw, w, reps: int = 7):
 
 
 def cpu_baseline(w, ids, seconds: float, policy: int = 0):
-    """The oracle, as it is, on the first requests of the same streams (its own rows from the generator)."""
+    """The oracle, as it is, on the first requests of the same streams (its own rows from the generator), on one
+    host core: the process is pinned to its first allowed core for this leg (and unpinned after). Timed with
+    perf_counter around the oracle's C calls; the sample's rows are drawn before the clock starts."""
     import numpy as np
     import oracle
     import workload
+    allowed = sorted(os.sched_getaffinity(0))
+    pinned = allowed[0]
+    os.sched_setaffinity(0, {pinned})
+    try:
+        rep = _cpu_baseline_pinned(w, ids, seconds, policy, np, oracle, workload)
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    rep["pinned_core"] = pinned
+    rep["available_cores"] = len(allowed)
+    rep["all_cores"] = _oracle_all_cores(w, rep.pop("_sample"), rep.pop("_host"), rep.pop("_tail"), rep.pop("_tail0"),
+                                         policy, ids.shape[1])
+    return rep
+
+
+def _cpu_baseline_pinned(w, ids, seconds, policy, np, oracle, workload):
     n_steps = ids.shape[1]
     # size the sample from a short calibration on one request
     cal = oracle.Oracle(1, w.buffer_slots, w.top_k, w.host_rows, w.row_bytes,
@@ -177,9 +211,10 @@ def cpu_baseline(w, ids, seconds: float, policy: int = 0):
     dt = time.perf_counter() - t0
     entries = n_req * n_steps * w.top_k
     rep = {"value": entries / dt, "unit": "entries/s", "cores": 1, "kind": "oracle",
-           "sample": f"{n_req} of {w.num_requests} requests x all {n_steps} steps ({dt:.1f} s, single thread)",
-           "miss_copy_GBps": misses * w.row_bytes / dt / 1e9}
-    rep["all_cores"] = _oracle_all_cores(w, sub, host, tail, tail0, policy, n_steps)
+           "sample": f"{n_req} of {w.num_requests} requests x all {n_steps} steps ({dt:.1f} s, single thread "
+                     f"pinned to one core)",
+           "miss_copy_GBps": misses * w.row_bytes / dt / 1e9,
+           "_sample": sub, "_host": host, "_tail": tail, "_tail0": tail0}
     return rep
 
 
@@ -251,7 +286,10 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step, hbm_c
     if status[W:].cpu().numpy().any():
         raise SystemExit("device status bits set during the split leg")
     mean_m = m.sum() / K
-    meta = R * (12 * k + 8 * B) + 12 * mean_m
+    # what a plan must move, per request: ids 4k, slot table 4B and order list 2B read; outputs 4k, order list 2B,
+    # stamps of the used slots (at most 4k) and the victims' slot-table entries 4m written; the miss list for
+    # the copy (token, slot, evicted token) 12m written
+    meta = R * (12 * k + 8 * B) + 16 * mean_m
     event_avg = float(plan_ms.mean())
     # The plans alone, back to back from a reset: a plan needs only the metadata the previous plan left (the
     # copies move bytes), so K plans in a row are the hit path run on its own. Two events around the chain
@@ -269,19 +307,49 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step, hbm_c
     if status[W:].cpu().numpy().any():
         raise SystemExit("device status bits set during the plan chain")
     same_chain = bool((miss[W:].cpu().numpy().astype(np.int64) == m).all())
-    plan_avg = c0.elapsed_time(c1) / K
+    eager_avg = c0.elapsed_time(c1) / K
+    # The same chain captured as one HIP graph and replayed once: the device runs the plans back to back with no
+    # host launch in between, so the figure is the GPU's and not the Python launch rate (the launch path checks
+    # every tensor argument, a few microseconds per call, close to a plan's own duration).
+    sw.reset()
+    for t in range(W):
+        hm.hs_plan(sw.ctx, topk[t], tail0, out, miss[t], status[t], plan, stream)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(K):
+            hm.hs_plan(sw.ctx, topk[W + i], tail0, out, miss[W + i], status[W + i], plan, side)
+    torch.cuda.synchronize()
+    miss[W:].zero_()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    if status[W:].cpu().numpy().any():
+        raise SystemExit("device status bits set during the captured plan chain")
+    same_chain = same_chain and bool((miss[W:].cpu().numpy().astype(np.int64) == m).all())
+    plan_avg = g0.elapsed_time(g1) / K
     hit_gbps = meta / (plan_avg / 1e3) / 1e9
     copy_gbps = mean_m * rb / (float(copy_ms.mean()) / 1e3) / 1e9
-    log(f"[bench] split: plan {event_avg * 1e3:.1f} us/step between copies, {plan_avg * 1e3:.1f} us back to back "
-        f"({hit_gbps:.0f} GB/s of metadata), copy {copy_ms.mean() * 1e3:.0f} us/step ({copy_gbps:.1f} GB/s), "
-        f"whole step {total_ms / K:.3f} ms")
-    return {"kernel": "resolve_kernel<plan> (hs_plan)", "bound": "hbm", "achieved": hit_gbps, "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s", "frac": hit_gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": meta,
+    log(f"[bench] split: plan {event_avg * 1e3:.1f} us/step between copies, {plan_avg * 1e3:.2f} us back to back in "
+        f"a graph ({eager_avg * 1e3:.2f} us launched one by one; {hit_gbps:.0f} GB/s of metadata), copy "
+        f"{copy_ms.mean() * 1e3:.0f} us/step ({copy_gbps:.1f} GB/s), whole step {total_ms / K:.3f} ms")
+    return {"kernel": "resolve_direct_kernel<plan> (hs_plan)", "bound": "hbm", "achieved": hit_gbps,
+            "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hit_gbps / HBM_PEAK_GBPS,
+            "algorithmic_bytes_per_launch": meta,
+            "bytes_model": "per request 12k + 8B + 16m (ids, slot table, order list, outputs, stamps, slot-table "
+                           "entries, miss list); the page-table updates ride with hs_copy",
             "frac_of_measured_hbm_copy": (hit_gbps / hbm_copy) if hbm_copy else None,
-            "avg_launch_us": plan_avg * 1e3, "timing": "K plans back to back between two events",
+            "avg_launch_us": plan_avg * 1e3,
+            "timing": "K plans back to back, captured as one HIP graph and replayed once between two events",
+            "avg_launch_us_eager_chain": eager_avg * 1e3,
             "avg_launch_us_between_copies": event_avg * 1e3, "p50_launch_us_between_copies": float(np.median(plan_ms)) * 1e3,
             "chain_same_misses": same_chain,
-            "traffic": measured_traffic(w.name, "resolve_plan"),
+            **traffic_fields(w.name, "resolve_plan", meta),
             "copy_kernel_avg_us": float(copy_ms.mean()) * 1e3, "copy_kernel_GBps": copy_gbps,
             "split_step_ms": total_ms / K, "same_misses_as_fused": bool(abs(mean_m - mean_miss_per_step) < 1e-6)}
 
@@ -333,6 +401,82 @@ def overlap_leg(hm, torch, np, sw, topk, tail0, W, K, w):
     log(f"[bench] overlapped split: {ms:.3f} ms/step ({K * R * k / (ms * K / 1e3) / 1e6:.1f} M entries/s)")
     return {"step_ms": ms, "entries_per_s": R * k / (ms / 1e3), "miss_copy_GBps": m.sum() * w.row_bytes / K / (ms / 1e3) / 1e9,
             "steps": K, "warmup": W, "gather": w.fused_gather}
+
+
+def overlap_compute_leg(hm, torch, np, sw, topk, tail0, W, K, w):
+    """The copy of a step on a second stream beside independent HBM-bound work on the launch stream, standing in
+    for the compute a decode step overlaps the swap-in I/O with: device-to-device copies of a 600 MB buffer,
+    repeated to last about as long as the row copy. (A gather of the resident rows would race with the copy's
+    writes into the victim slots, so the stand-in touches none of the library's buffers.) Each step is timed
+    three ways: the copy alone, the HBM work alone, and both launched together."""
+    R, k, rb = w.num_requests, w.top_k, w.row_bytes
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    sw.reset()
+    plan = sw.plan_buffer()
+    out = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    miss = torch.zeros((R,), dtype=torch.int32, device="cuda")
+    status = torch.zeros((R,), dtype=torch.int32, device="cuda")
+    src = torch.empty(600 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+
+    def timed(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(main)
+        fn()
+        b.record(main)
+        b.synchronize()
+        return a.elapsed_time(b)
+
+    for t in range(W):
+        hm.hs_plan(sw.ctx, topk[t], tail0, out, miss, status, plan, main)
+        hm.hs_copy(sw.ctx, plan, miss, stream=main)
+    torch.cuda.synchronize()
+    one = timed(lambda: dst.copy_(src))
+    copies = []
+    for t in range(W, W + 3):  # the copy's duration at this point of the stream sizes the HBM work
+        hm.hs_plan(sw.ctx, topk[t], tail0, out, miss, status, plan, main)
+        copies.append(timed(lambda: hm.hs_copy(sw.ctx, plan, miss, stream=main)))
+    reps = max(1, int(round(float(np.median(copies)) / one)))
+
+    def hbm_work():
+        for _ in range(reps):
+            dst.copy_(src)
+
+    def both():
+        start = torch.cuda.Event()
+        start.record(main)
+        side.wait_event(start)
+        hm.hs_copy(sw.ctx, plan, miss, stream=side)
+        done = torch.cuda.Event()
+        done.record(side)
+        hbm_work()
+        main.wait_event(done)
+
+    alone, work, together = [], [], []
+    n = min(K, 3 * 16)
+    for i in range(n):
+        t = W + 3 + i
+        hm.hs_plan(sw.ctx, topk[t], tail0, out, miss, status, plan, main)
+        if i % 3 == 0:
+            alone.append(timed(lambda: hm.hs_copy(sw.ctx, plan, miss, stream=main)))
+        elif i % 3 == 1:
+            work.append(timed(hbm_work))
+            hm.hs_copy(sw.ctx, plan, miss, stream=main)
+        else:
+            together.append(timed(both))
+    del src, dst
+    ca, wa, tg = float(np.median(alone)), float(np.median(work)), float(np.median(together))
+    log(f"[bench] copy beside HBM work: copy {ca:.3f} ms, HBM work {wa:.3f} ms ({reps} x 1.2 GB moved), "
+        f"together {tg:.3f} ms = {tg / max(ca, wa):.3f} x the longer")
+    return {"copy_ms": ca, "hbm_work_ms": wa, "together_ms": tg, "together_over_longer": tg / max(ca, wa),
+            "together_over_sum": tg / (ca + wa), "hbm_work": f"{reps} device-to-device copies of 600 MB",
+            "hbm_work_GBps": reps * 2 * src_bytes(600) / (wa / 1e3) / 1e9, "copy_workgroups": 64,
+            "steps": n, "timing": "medians of steps timed one way each, in rotation"}
+
+
+def src_bytes(mib: int) -> int:
+    return mib << 20
 
 
 def graph_leg(hm, torch, np, sw, topk, tail0, W, K, w, eager_miss):
@@ -397,7 +541,7 @@ def gather_leg(hm, torch, np, sw, out, w, n, hbm_copy):
             "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS, "algorithmic_bytes_per_launch": algo,
             "avg_launch_us": avg * 1e3, "p50_launch_us": float(np.median(ms)) * 1e3, "launches": n,
             "frac_of_measured_hbm_copy": (gbps / hbm_copy) if hbm_copy else None,
-            "traffic": measured_traffic(w.name, "gather")}
+            **traffic_fields(w.name, "gather", algo)}
 
 
 def _timed_launches(torch, np, n, warm, launch):
@@ -706,9 +850,10 @@ def main() -> int:
         "cold_step0_misses_per_request": float(miss[0].float().mean().item()) if W else None,
         "measured_d2h_link_GBps": d2h_peak,
         "roofline": {"bound": "host_link", "achieved": miss_gbps, "peak": PCIE5_X16_GBPS, "unit": "GB/s",
-                     "frac": miss_gbps / PCIE5_X16_GBPS, "traffic": measured_traffic(w.name, "resolve_fused"),
-                     "kernel": "resolve_kernel",
-                     "algorithmic_bytes_per_launch": miss_bytes / K},
+                     "frac": miss_gbps / PCIE5_X16_GBPS,
+                     "kernel": "resolve_direct_kernel<fused> (hs_resolve)" if T == 0 else "resolve_kernel<fused> (hs_resolve)",
+                     "algorithmic_bytes_per_launch": miss_bytes / K,
+                     **traffic_fields(w.name, "resolve_fused", miss_bytes / K + hbm_bytes)},
         "hbm": {"achieved": hbm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hbm_gbps / HBM_PEAK_GBPS,
                 "algorithmic_bytes_per_launch": hbm_bytes},
     }
@@ -722,6 +867,9 @@ def main() -> int:
                                     w, total_miss / K, hbm_copy)
     if args.split_steps != 0:
         rep["overlap"] = overlap_leg(hm, torch, np, sw, topk, tail0, W, K if args.split_steps < 0 else args.split_steps, w)
+        if not w.fused_gather:
+            rep["overlap_with_compute"] = overlap_compute_leg(hm, torch, np, sw, topk, tail0, W,
+                                                              K if args.split_steps < 0 else args.split_steps, w)
     if args.trial_steps > 0:
         kt = min(args.trial_steps, K)
         rep["trial_commit"] = trial_leg(hm, torch, np, sw, topk, tail0, W, kt, w)

@@ -457,6 +457,7 @@ int hs_copy(hs_ctx* ctx, const int32_t* d_plan, const int32_t* d_miss, void* d_g
   a.T = ctx->cfg.tail_tokens;
   a.row16 = ctx->cfg.row_bytes / 16;
   a.rows = std::max(1, hs::kGatherChunks / a.row16);
+  a.workgroups = hs::kCopyWorkgroups;
   a.plan = d_plan;
   a.miss = d_miss;
   a.host = (const hs::v4u*)ctx->pool_dev;

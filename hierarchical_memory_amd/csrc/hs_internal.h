@@ -170,6 +170,7 @@ struct CommitArgs {
 struct CopyArgs {
   int32_t R, k, B, H, T, row16;
   int32_t rows;         // with a gather: selected rows per workgroup
+  int32_t workgroups;   // without a gather: workgroups of the copy (each takes every workgroups-th request)
   const int32_t* plan;  // [R][4][k]
   const int32_t* miss;  // [R]
   const v4u* host;
@@ -218,6 +219,11 @@ struct ResetArgs {
   int32_t* step;
   int32_t* epoch;      // [R] change counters, advanced (nullptr: leave them)
 };
+
+// copy_kernel: 16-byte host loads each thread keeps in flight, and the default number of workgroups (a
+// measured point where the host link is already saturated, leaving most compute units to other work)
+constexpr int kCopyUnroll = 8;
+constexpr int kCopyWorkgroups = 64;
 
 // gather_kernel: threads per workgroup, 16-byte loads in flight per thread, and the chunks one workgroup
 // covers (its row count is the largest that fits, at least one)

@@ -1214,28 +1214,44 @@ __device__ __forceinline__ void plan_page_updates(const CopyArgs& a, int r, int 
   }
 }
 
-// Rows of a plan: workgroup (g, r) copies every gridDim.x-th group of 16-byte chunks of request r's
-// missed rows from the pinned host pool into their victim slots, one load in flight per thread, and then its
-// share of the plan's page-table updates.
+// Rows of a plan on a bounded grid: workgroup w copies the missed rows of requests w, w + gridDim.x, ... from
+// the pinned host pool into their victim slots, flattened over (miss, 16-byte chunk), each thread keeping
+// kCopyUnroll host loads in flight; then it applies those requests' page-table updates. About 128K loads in
+// flight over the chip saturate the host link, so a few dozen workgroups reach its rate and leave the other
+// compute units to concurrent work.
 __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
-  const int r = blockIdx.y;
-  const int m = a.miss[r];
-  if (m <= 0 || m > a.k) return;
   const int row16 = a.row16;
-  const int total = m * row16;
-  const size_t rk = (size_t)r * a.k;
-  const int32_t* ptok = a.plan + rk * 4;
-  const int32_t* pslot = ptok + a.k;
-  const v4u* hostr = a.host + (size_t)r * a.H * row16;
-  v4u* hotr = a.hot + (size_t)r * a.B * row16;
-  const int stride = gridDim.x * blockDim.x;
-  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < total; c += stride) {
-    const int j = c / row16, q = c - j * row16;
-    const int x = ptok[j], s = pslot[j];
-    if (x >= 0 && x < a.H && s >= 0 && s < a.B)
-      hotr[(size_t)s * row16 + q] = load_host(hostr + (size_t)x * row16 + q);
+  for (int r = blockIdx.x; r < a.R; r += gridDim.x) {
+    const int m = a.miss[r];
+    if (m <= 0 || m > a.k) continue;
+    const int total = m * row16;
+    const size_t rk = (size_t)r * a.k;
+    const int32_t* ptok = a.plan + rk * 4;
+    const int32_t* pslot = ptok + a.k;
+    const v4u* hostr = a.host + (size_t)r * a.H * row16;
+    v4u* hotr = a.hot + (size_t)r * a.B * row16;
+    for (int c0 = threadIdx.x; c0 < total; c0 += 256 * kCopyUnroll) {
+      v4u v[kCopyUnroll];
+      int64_t dst[kCopyUnroll];
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u) {
+        const int c = c0 + u * 256;
+        dst[u] = -1;
+        if (c < total) {
+          const int j = c / row16, q = c - j * row16;
+          const int x = ptok[j], s = pslot[j];
+          if (x >= 0 && x < a.H && s >= 0 && s < a.B) {
+            v[u] = load_host(hostr + (size_t)x * row16 + q);
+            dst[u] = (int64_t)s * row16 + q;
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kCopyUnroll; ++u)
+        if (dst[u] >= 0) hotr[dst[u]] = v[u];
+    }
+    plan_page_updates(a, r, m, threadIdx.x, 256);
   }
-  plan_page_updates(a, r, m, blockIdx.x * blockDim.x + threadIdx.x, stride);
 }
 
 // A plan's rows and the gather of every selected row, in the gather kernel's tiles: workgroup (b, r) fills
@@ -1569,11 +1585,8 @@ hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(copy_gather_kernel, dim3(bx, (unsigned)a.R), dim3(kGatherThreads), 0, s, a);
     return hipGetLastError();
   }
-  // about 128K threads (one 16-byte host load in flight each) over the whole chip
-  int g = (512 + a.R - 1) / a.R;
-  if (g < 1) g = 1;
-  if (g > 512) g = 512;
-  hipLaunchKernelGGL(copy_kernel, dim3(g, a.R), dim3(256), 0, s, a);
+  const int g = a.workgroups < 1 ? 1 : a.workgroups > a.R ? a.R : a.workgroups;
+  hipLaunchKernelGGL(copy_kernel, dim3(g), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -136,10 +136,21 @@ def hs_required_sizes(cfg: HsConfig) -> HsSizes:
     return s
 
 
-# Sizes of every live context, by its address: the calls below check each tensor against them (dtype and
+class _Limits:
+    """What a context's calls need of their tensor arguments, computed once at hs_create: element counts of
+    the int32 arrays and byte counts of the row buffers."""
+    __slots__ = ("R", "RK", "plan", "gather", "trial", "row_bytes")
+
+    def __init__(self, cfg: HsConfig, s: HsSizes):
+        self.R, self.RK = cfg.num_requests, cfg.num_requests * cfg.top_k
+        self.plan, self.gather, self.trial = s.plan_bytes // 4, s.gather_bytes, s.trial_bytes
+        self.row_bytes = cfg.row_bytes
+
+
+# Limits of every live context, by its address: the calls below check each tensor against them (dtype and
 # element count, from tensor metadata only) before a pointer reaches the library, whose C calls take raw
 # pointers and cannot.
-_CTX_SIZES: Dict[int, Tuple[HsConfig, HsSizes]] = {}
+_CTX_SIZES: Dict[int, _Limits] = {}
 
 
 def _ctx_key(ctx) -> int:
@@ -148,10 +159,14 @@ def _ctx_key(ctx) -> int:
     return int(ctx.value or 0) if isinstance(ctx, ctypes.c_void_p) else int(ctx)
 
 
+def _register(ctx, cfg: HsConfig, sizes: HsSizes) -> None:
+    _CTX_SIZES[_ctx_key(ctx)] = _Limits(cfg, sizes)
+
+
 def hs_create(cfg: HsConfig) -> ctypes.c_void_p:
     ctx = ctypes.c_void_p()
     _check(lib().hs_create(ctypes.byref(cfg), ctypes.byref(ctx)))
-    _CTX_SIZES[_ctx_key(ctx)] = (cfg, hs_required_sizes(cfg))
+    _register(ctx, cfg, hs_required_sizes(cfg))
     return ctx
 
 
@@ -161,30 +176,34 @@ def hs_host_pool(ctx) -> Tuple[int, int, int]:
     return base.value, stride.value, rows.value
 
 
-def _arg(name: str, t, ctx, *, int32: bool = True, count=None, nbytes=None, nullable: bool = False):
-    """Checks one tensor argument from its metadata and returns it (None when absent). int32 index arrays must be
-    torch.int32; row buffers may have any dtype but must hold nbytes. count / nbytes are functions of the
-    context's (config, sizes); without a known context only the dtype is checked (the library then refuses the
-    context)."""
+_INT32 = None
+
+
+def _arg(name: str, t, lim: Optional[_Limits], count: int = 0, nbytes: int = 0, int32: bool = True,
+         nullable: bool = False):
+    """Checks one tensor argument from its metadata and returns it (None when absent): int32 index arrays must
+    be torch.int32 with at least count elements; row buffers may have any dtype but must hold nbytes. Without a
+    known context (lim None) only the dtype is checked (the library then refuses the context)."""
     if t is None:
         if nullable:
             return None
         raise ValueError(f"{name} must not be None")
-    import torch
-    if int32 and t.dtype != torch.int32:
+    if int32 and t.dtype is not _INT32:
         raise ValueError(f"{name} must be a torch.int32 tensor, got {t.dtype}")
-    info = _CTX_SIZES.get(_ctx_key(ctx))
-    if info is not None:
-        if count is not None and t.numel() < count(*info):
-            raise ValueError(f"{name} has {t.numel()} elements, the context needs at least {count(*info)}")
-        have = t.numel() * t.element_size()
-        if nbytes is not None and have < nbytes(*info):
-            raise ValueError(f"{name} has {have} bytes, the context needs at least {nbytes(*info)}")
+    if lim is not None:
+        if count and t.numel() < count:
+            raise ValueError(f"{name} has {t.numel()} elements, the context needs at least {count}")
+        if nbytes and t.numel() * t.element_size() < nbytes:
+            raise ValueError(f"{name} has {t.numel() * t.element_size()} bytes, the context needs at least {nbytes}")
     return t
 
 
-_R = lambda c, s: c.num_requests  # noqa: E731
-_RK = lambda c, s: c.num_requests * c.top_k  # noqa: E731
+def _lim(ctx) -> Optional[_Limits]:
+    global _INT32
+    if _INT32 is None:
+        import torch
+        _INT32 = torch.int32
+    return _CTX_SIZES.get(_ctx_key(ctx))
 
 
 def _ptr(t) -> Optional[int]:
@@ -228,55 +247,58 @@ def _ptrs(*tensors):
 
 def hs_reset(ctx, request_ids=None, stream=None) -> None:
     n = -1 if request_ids is None else request_ids.numel()
-    (ids,) = _ptrs(_arg("request_ids", request_ids, ctx, nullable=True))
+    (ids,) = _ptrs(_arg("request_ids", request_ids, _lim(ctx), nullable=True))
     _check(lib().hs_reset(ctx, ids, n, _stream(stream)))
 
 
-def _step_args(ctx, topk, tail0, out, miss, status, gather, gather_required=False):
-    return (_arg("topk", topk, ctx, count=_RK), _arg("tail0", tail0, ctx, count=_R, nullable=True),
-            _arg("out", out, ctx, count=_RK), _arg("miss", miss, ctx, count=_R), _arg("status", status, ctx, count=_R),
-            _arg("gather", gather, ctx, int32=False, nbytes=lambda c, s: s.gather_bytes,
+def _step_args(lim, topk, tail0, out, miss, status, gather, gather_required=False):
+    R, RK = (lim.R, lim.RK) if lim is not None else (0, 0)
+    return (_arg("topk", topk, lim, RK), _arg("tail0", tail0, lim, R, nullable=True), _arg("out", out, lim, RK),
+            _arg("miss", miss, lim, R), _arg("status", status, lim, R),
+            _arg("gather", gather, lim, nbytes=lim.gather if lim is not None else 0, int32=False,
                  nullable=not gather_required))
 
 
-def _plan_arg(ctx, plan):
-    return _arg("plan", plan, ctx, count=lambda c, s: s.plan_bytes // 4)
-
-
 def hs_resolve(ctx, topk, tail0, out, miss, status, gather=None, stream=None) -> None:
-    _check(lib().hs_resolve(ctx, *_ptrs(*_step_args(ctx, topk, tail0, out, miss, status, gather)), _stream(stream)))
+    _check(lib().hs_resolve(ctx, *_ptrs(*_step_args(_lim(ctx), topk, tail0, out, miss, status, gather)),
+                            _stream(stream)))
 
 
 def hs_plan(ctx, topk, tail0, out, miss, status, plan, stream=None, row_sources: bool = False) -> None:
     """row_sources: also record each position's row source, which a gathering hs_copy of this plan needs."""
-    a = _ptrs(*_step_args(ctx, topk, tail0, out, miss, status, None)[:5], _plan_arg(ctx, plan))
+    lim = _lim(ctx)
+    a = _ptrs(*_step_args(lim, topk, tail0, out, miss, status, None)[:5],
+              _arg("plan", plan, lim, lim.plan if lim is not None else 0))
     _check(lib().hs_plan(ctx, *a, HS_PLAN_ROW_SOURCES if row_sources else 0, _stream(stream)))
 
 
 def hs_copy(ctx, plan, miss, gather=None, stream=None) -> None:
-    a = _ptrs(_plan_arg(ctx, plan), _arg("miss", miss, ctx, count=_R),
-              _arg("gather", gather, ctx, int32=False, nbytes=lambda c, s: s.gather_bytes, nullable=True))
+    lim = _lim(ctx)
+    a = _ptrs(_arg("plan", plan, lim, lim.plan if lim is not None else 0),
+              _arg("miss", miss, lim, lim.R if lim is not None else 0),
+              _arg("gather", gather, lim, nbytes=lim.gather if lim is not None else 0, int32=False, nullable=True))
     _check(lib().hs_copy(ctx, *a, _stream(stream)))
 
 
 def hs_step_static(ctx, topk, tail0, out, miss, status, gather=None, stream=None) -> None:
     """hs_plan + hs_copy in one call with the plan in the library's static device array (allocates nothing)."""
-    _check(lib().hs_step_static(ctx, *_ptrs(*_step_args(ctx, topk, tail0, out, miss, status, gather)),
+    _check(lib().hs_step_static(ctx, *_ptrs(*_step_args(_lim(ctx), topk, tail0, out, miss, status, gather)),
                                 _stream(stream)))
 
 
-def _trial_arg(ctx, trial):
-    return _arg("trial", trial, ctx, nbytes=lambda c, s: s.trial_bytes)
-
-
 def hs_trial(ctx, topk, tail0, out, miss, status, gather, trial, stream=None) -> None:
-    a = _ptrs(*_step_args(ctx, topk, tail0, out, miss, status, gather, gather_required=True), _trial_arg(ctx, trial))
+    lim = _lim(ctx)
+    a = _ptrs(*_step_args(lim, topk, tail0, out, miss, status, gather, gather_required=True),
+              _arg("trial", trial, lim, nbytes=lim.trial if lim is not None else 0))
     _check(lib().hs_trial(ctx, *a, _stream(stream)))
 
 
 def hs_commit(ctx, trial, gather, accept=None, status=None, stream=None) -> None:
-    a = _ptrs(_trial_arg(ctx, trial), _arg("gather", gather, ctx, int32=False, nbytes=lambda c, s: s.gather_bytes),
-              _arg("accept", accept, ctx, count=_R, nullable=True), _arg("status", status, ctx, count=_R, nullable=True))
+    lim = _lim(ctx)
+    R = lim.R if lim is not None else 0
+    a = _ptrs(_arg("trial", trial, lim, nbytes=lim.trial if lim is not None else 0),
+              _arg("gather", gather, lim, nbytes=lim.gather if lim is not None else 0, int32=False),
+              _arg("accept", accept, lim, R, nullable=True), _arg("status", status, lim, R, nullable=True))
     _check(lib().hs_commit(ctx, *a, _stream(stream)))
 
 
@@ -285,41 +307,42 @@ def hs_offload(ctx, rows, pos, status=None, stream=None) -> None:
     int32 [R]."""
     if rows is None:
         raise ValueError("rows must not be None")
-    info = _CTX_SIZES.get(_ctx_key(ctx))
+    lim = _lim(ctx)
     if rows.dim() != 3:
         raise ValueError(f"rows must be [requests, n, row] (3 dimensions), got shape {tuple(rows.shape)}")
-    if info is not None:
-        cfg = info[0]
-        if rows.shape[0] != cfg.num_requests or rows.shape[2] * rows.element_size() != cfg.row_bytes:
-            raise ValueError(f"rows must be [{cfg.num_requests}, n, {cfg.row_bytes} bytes], got shape "
-                             f"{tuple(rows.shape)} of {rows.dtype}")
-    a = _ptrs(_arg("rows", rows, ctx, int32=False), _arg("pos", pos, ctx, count=_R),
-              _arg("status", status, ctx, count=_R, nullable=True))
+    if lim is not None and (rows.shape[0] != lim.R or rows.shape[2] * rows.element_size() != lim.row_bytes):
+        raise ValueError(f"rows must be [{lim.R}, n, {lim.row_bytes} bytes], got shape {tuple(rows.shape)} of "
+                         f"{rows.dtype}")
+    R = lim.R if lim is not None else 0
+    a = _ptrs(_arg("rows", rows, lim, int32=False), _arg("pos", pos, lim, R),
+              _arg("status", status, lim, R, nullable=True))
     _check(lib().hs_offload(ctx, a[0], a[1], int(rows.shape[1]), a[2], _stream(stream)))
 
 
 def hs_advance_tail(ctx, tail0, n, status=None, stream=None) -> None:
     """tail0: device int32 [R], advanced in place; n: device int32 [R]."""
-    a = _ptrs(_arg("tail0", tail0, ctx, count=_R), _arg("n", n, ctx, count=_R),
-              _arg("status", status, ctx, count=_R, nullable=True))
+    lim = _lim(ctx)
+    R = lim.R if lim is not None else 0
+    a = _ptrs(_arg("tail0", tail0, lim, R), _arg("n", n, lim, R), _arg("status", status, lim, R, nullable=True))
     _check(lib().hs_advance_tail(ctx, *a, _stream(stream)))
 
 
 def hs_gather(ctx, out, gather, stream=None) -> None:
-    a = _ptrs(_arg("out", out, ctx, count=_RK),
-              _arg("gather", gather, ctx, int32=False, nbytes=lambda c, s: s.gather_bytes))
+    lim = _lim(ctx)
+    a = _ptrs(_arg("out", out, lim, lim.RK if lim is not None else 0),
+              _arg("gather", gather, lim, nbytes=lim.gather if lim is not None else 0, int32=False))
     _check(lib().hs_gather(ctx, *a, _stream(stream)))
 
 
 def hs_export_state(ctx, dst, what: int = 3, stream=None) -> None:
     """dst: a device tensor of at least state_tables_bytes / state_rows_bytes (as what selects); the library
     checks its byte size."""
-    (p,) = _ptrs(_arg("dst", dst, ctx, int32=False))
+    (p,) = _ptrs(_arg("dst", dst, _lim(ctx), int32=False))
     _check(lib().hs_export_state(ctx, p, _bytes(dst), what, _stream(stream)))
 
 
 def hs_import_state(ctx, src, what: int = 3, stream=None) -> None:
-    (p,) = _ptrs(_arg("src", src, ctx, int32=False))
+    (p,) = _ptrs(_arg("src", src, _lim(ctx), int32=False))
     _check(lib().hs_import_state(ctx, p, _bytes(src), what, _stream(stream)))
 
 

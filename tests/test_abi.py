@@ -188,7 +188,7 @@ def fake_ctx():
     checks run; no call below gets past them to the library."""
     cfg = hm.config(3, 8, 16, 0.0, 64, 100, 4)
     key = 0x5EED0000
-    hm.hisparse._CTX_SIZES[key] = (cfg, hm.hs_required_sizes(cfg))
+    hm.hisparse._register(key, cfg, hm.hs_required_sizes(cfg))
     yield ctypes.c_void_p(key)
     hm.hisparse._CTX_SIZES.pop(key, None)
 
