@@ -224,6 +224,7 @@ struct ResetArgs {
 // measured point where the host link is already saturated, leaving most compute units to other work)
 constexpr int kCopyUnroll = 8;
 constexpr int kCopyWorkgroups = 64;
+constexpr int kCopyThreads = 256;
 
 // gather_kernel: threads per workgroup, 16-byte loads in flight per thread, and the chunks one workgroup
 // covers (its row count is the largest that fits, at least one)

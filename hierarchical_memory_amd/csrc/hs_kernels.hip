@@ -1226,7 +1226,7 @@ __device__ __forceinline__ void plan_page_updates(const CopyArgs& a, int r, int 
 // kCopyUnroll host loads in flight; then it applies those requests' page-table updates. About 128K loads in
 // flight over the chip saturate the host link, so a few dozen workgroups reach its rate and leave the other
 // compute units to concurrent work.
-__global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
+__global__ __launch_bounds__(kCopyThreads) void copy_kernel(CopyArgs a) {
   const int row16 = a.row16;
   for (int r = blockIdx.x; r < a.R; r += gridDim.x) {
     const int m = a.miss[r];
@@ -1237,12 +1237,12 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
     const int32_t* pslot = ptok + a.k;
     const v4u* hostr = a.host + (size_t)r * a.H * row16;
     v4u* hotr = a.hot + (size_t)r * a.B * row16;
-    for (int c0 = threadIdx.x; c0 < total; c0 += 256 * kCopyUnroll) {
+    for (int c0 = threadIdx.x; c0 < total; c0 += kCopyThreads * kCopyUnroll) {
       v4u v[kCopyUnroll];
       int64_t dst[kCopyUnroll];
 #pragma unroll
       for (int u = 0; u < kCopyUnroll; ++u) {
-        const int c = c0 + u * 256;
+        const int c = c0 + u * kCopyThreads;
         dst[u] = -1;
         if (c < total) {
           const int j = c / row16, q = c - j * row16;
@@ -1257,7 +1257,7 @@ __global__ __launch_bounds__(256) void copy_kernel(CopyArgs a) {
       for (int u = 0; u < kCopyUnroll; ++u)
         if (dst[u] >= 0) hotr[dst[u]] = v[u];
     }
-    plan_page_updates(a, r, m, threadIdx.x, 256);
+    plan_page_updates(a, r, m, threadIdx.x, kCopyThreads);
   }
 }
 
@@ -1593,7 +1593,7 @@ hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const int g = a.workgroups < 1 ? 1 : a.workgroups > a.R ? a.R : a.workgroups;
-  hipLaunchKernelGGL(copy_kernel, dim3(g), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(copy_kernel, dim3(g), dim3(kCopyThreads), 0, s, a);
   return hipGetLastError();
 }
 
