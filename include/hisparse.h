@@ -244,9 +244,10 @@ int hs_step_static(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, i
  * hs_commit applies the records of the requests with d_accept[r] != 0 (all when d_accept is NULL): LRU
  * order, stamps, slot and page tables, step counter, and the missed rows copied from d_gather into their
  * victim slots (HBM to HBM). Requests not accepted keep their state, so a trial is rolled back by not
- * committing it and retried by calling hs_trial again. A record planned at another step than the
- * request's current one is not applied and sets HS_STATUS_STALE in d_status[r] (optional, [R]). d_gather
- * must still hold what hs_trial wrote.
+ * committing it and retried by calling hs_trial again. A record made at another step than the request's
+ * current one, or before a reset, offload, tail advance or state import of that request (the change counter
+ * in hs_device_views.epoch differs), is not applied and sets HS_STATUS_STALE in d_status[r] (optional, [R]).
+ * d_gather must still hold what hs_trial wrote.
  */
 int hs_trial(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
              int32_t* d_status, void* d_gather, int32_t* d_trial, void* stream);
