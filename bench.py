@@ -255,6 +255,13 @@ def _oracle_all_cores(w, sub, host, tail, tail0, policy, n_steps):
             "sample": f"the same {n_req} requests x {n_steps} steps on {cores} threads ({dt:.1f} s)", "cpu_model": model}
 
 
+def resolve_kernel_name(sw, mode: str, gather: bool) -> str:
+    """The resolve kernel a launch of this shape runs: the direct layout (token -> slot table in LDS) where it
+    fits, else the rank layout; the library decides per shape, separately for launches with a gather output."""
+    direct = sw.sizes.token_slot_table & (2 if gather else 1)
+    return f"{'resolve_direct_kernel' if direct else 'resolve_kernel'}<{mode}>"
+
+
 def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step, hbm_copy=None):
     """The same stream again from a reset, as hs_plan + hs_copy on one stream. The plan kernel carries all the
     metadata work of a step (hit test, ranks, victims, page/slot tables, stamps, outputs) and no rows, so its
@@ -338,7 +345,7 @@ def split_leg(hm, torch, np, sw, topk, tail0, W, K, w, mean_miss_per_step, hbm_c
     log(f"[bench] split: plan {event_avg * 1e3:.1f} us/step between copies, {plan_avg * 1e3:.2f} us back to back in "
         f"a graph ({eager_avg * 1e3:.2f} us launched one by one; {hit_gbps:.0f} GB/s of metadata), copy "
         f"{copy_ms.mean() * 1e3:.0f} us/step ({copy_gbps:.1f} GB/s), whole step {total_ms / K:.3f} ms")
-    return {"kernel": "resolve_direct_kernel<plan> (hs_plan)", "bound": "hbm", "achieved": hit_gbps,
+    return {"kernel": resolve_kernel_name(sw, "plan", False) + " (hs_plan)", "bound": "hbm", "achieved": hit_gbps,
             "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hit_gbps / HBM_PEAK_GBPS,
             "algorithmic_bytes_per_launch": meta,
             "bytes_model": "per request 12k + 8B + 16m (ids, slot table, order list, outputs, stamps, slot-table "
@@ -851,7 +858,7 @@ def main() -> int:
         "measured_d2h_link_GBps": d2h_peak,
         "roofline": {"bound": "host_link", "achieved": miss_gbps, "peak": PCIE5_X16_GBPS, "unit": "GB/s",
                      "frac": miss_gbps / PCIE5_X16_GBPS,
-                     "kernel": "resolve_direct_kernel<fused> (hs_resolve)" if T == 0 else "resolve_kernel<fused> (hs_resolve)",
+                     "kernel": resolve_kernel_name(sw, "fused", w.fused_gather) + " (hs_resolve)",
                      "algorithmic_bytes_per_launch": miss_bytes / K,
                      **traffic_fields(w.name, "resolve_fused", miss_bytes / K + hbm_bytes)},
         "hbm": {"achieved": hbm_gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": hbm_gbps / HBM_PEAK_GBPS,

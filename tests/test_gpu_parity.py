@@ -740,6 +740,46 @@ def test_commit_after_an_offload_or_reset_is_stale():
     p.close()
 
 
+def test_commit_after_a_tail_advance_or_an_import_is_stale():
+    """A trial made before a tail advance that moves the windows, or before a state import (even of the very
+    state the trial was made from), is refused at commit (HS_STATUS_STALE) and leaves the state as the advance
+    or the import left it; the run then continues in parity."""
+    import hierarchical_memory_amd as hm
+    w = workload.HYBRID_64.with_(num_requests=4, steps=12)
+    p = Pair(w, gather=True)
+    R = w.num_requests
+    trial = p.sw.trial_buffer()
+    out, miss, status, g = p.outs
+    cstat = torch.full((R,), -1, dtype=torch.int32, device="cuda")
+    for _ in range(4):
+        p.step()
+    hm.hs_trial(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(p.ids[:, 4])).cuda(), p.tail0_dev, out, miss,
+                status, g, trial)
+    n = np.full(R, 16, np.int32)
+    hm.hs_advance_tail(p.sw.ctx, p.tail0_dev, torch.from_numpy(n).cuda())
+    t0_o = np.ascontiguousarray(p.tail0[p.sample])
+    p.o.advance_tail(t0_o, n[p.sample])
+    hm.hs_commit(p.sw.ctx, trial, g, None, cstat)
+    assert (cstat.cpu().numpy() == hm.HS_STATUS_STALE).all()
+    p.tail0 = p.tail0_dev.cpu().numpy().astype(np.int32)
+    assert (p.tail0[p.sample] == t0_o).all()
+    p.check_state()  # the advance's state: no trial applied
+    p.step(check_state=True)
+    # an import of the current state itself: a trial made before it is still stale
+    snap = p.sw.state_buffer(hm.HS_STATE_TABLES)
+    hm.hs_trial(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(p.ids[:, p.t])).cuda(), p.tail0_dev, out, miss,
+                status, g, trial)
+    hm.hs_export_state(p.sw.ctx, snap, hm.HS_STATE_TABLES)
+    hm.hs_import_state(p.sw.ctx, snap, hm.HS_STATE_TABLES)
+    cstat.fill_(-1)
+    hm.hs_commit(p.sw.ctx, trial, g, None, cstat)
+    assert (cstat.cpu().numpy() == hm.HS_STATUS_STALE).all()
+    p.check_state()
+    for _ in range(2):
+        p.step(check_state=True)
+    p.close()
+
+
 def test_import_tables_and_rebuild_order():
     """Tables computed elsewhere (here by the oracle, on the CPU) are imported without an order list;
     hs_rebuild_order derives it from the stamps and the run continues in parity."""
