@@ -61,6 +61,19 @@ constexpr int kMiscScanSel = 0, kMiscScanRank = kWaves, kMiscScanTail = 2 * kWav
               kMiscRepeat = 8 * kWaves + 1, kMiscBad = 8 * kWaves + 2, kMiscDummy = 8 * kWaves + 4;
 static_assert(kMiscDummy + 4 <= kMiscWords, "misc words (the dummy takes 16 bytes)");
 
+// The tail is a ring of T rows, token x in row x mod T. For a resident x (t0 <= x < t0 + T) that row is
+// (t0 mod T + (x - t0)) mod T: ring_base gives t0 mod T (0 without a tail), once per wave on uniform values,
+// and ring_row wraps the sum, which stays below 2T, once.
+__device__ __forceinline__ uint32_t ring_base(bool has_tail, int32_t t0, int32_t T) {
+  if (!has_tail || T <= 0) return 0u;
+  const int32_t m = t0 % T;
+  return (uint32_t)(m < 0 ? m + T : m);
+}
+__device__ __forceinline__ uint32_t ring_row(uint32_t base, uint32_t offset, int32_t T) {
+  const uint32_t e = base + offset;
+  return e >= (uint32_t)T ? e - (uint32_t)T : e;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2, 4, 8 inside each row of 16
 // lanes, then the row broadcasts of lane 15 (into rows 1 and 3) and lane 31 (into rows 2 and 3).
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -607,6 +620,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     }
   }
   __syncthreads();
+  const uint32_t t0m = ring_base(has_tail, t0, T);  // x mod T = (t0m + x - t0) mod T for a resident x
 
   // ---- phase 4: pair misses with victims: outputs and page table; the victims' new tokens go to the LDS
   // copy of the slot table, written back below as coalesced rows
@@ -643,7 +657,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       o = hit;
       g = o;
     } else if (c == C_RES) {
-      o = B + x % T;  // the tail is a ring: token x in row x mod T
+      o = B + (int32_t)ring_row(t0m, (uint32_t)x - (uint32_t)t0, T);  // the tail is a ring: x in row x mod T
       g = o;
     }
     at(out_r, i) = o;
@@ -813,6 +827,9 @@ __global__ __launch_bounds__(kThreads) void resolve_direct_kernel(ResolveArgs a)
 #pragma unroll
     for (int q = 0; q < kQ; ++q) sq[q] = ld128(stamp_b, 4u * (uint32_t)(s0 + 4 * q));
   }
+  // the ring row of a resident id x is x mod T = (t0 mod T + (x - t0)) mod T: one modulo per wave, on uniform
+  // values, instead of one per id (none without a tail)
+  const uint32_t t0m = ring_base(has_tail, t0, T);
   // scratch cleared while the loads are in flight: the missed-id and resident-id bitmaps (adjacent; at most
   // two 16-byte stores per thread), and this chunk's slot flags
   {
@@ -1055,7 +1072,7 @@ __global__ __launch_bounds__(kThreads) void resolve_direct_kernel(ResolveArgs a)
       const int i = tid + u * kThreads;
       const bool pos = i < k;
       // the output: a miss's victim, a hit's slot, a resident id's ring row B + x mod T, else -1
-      int32_t ov = res[u] ? B + x[u] % (T > 0 ? T : 1) : -1;
+      int32_t ov = res[u] ? B + (int32_t)ring_row(t0m, (uint32_t)x[u] - (uint32_t)t0, T) : -1;
       ov = hit[u] ? (int32_t)hs[u] : ov;
       ov = mi[u] ? v[u] : ov;
       const int32_t g = mi[u] ? -2 - j[u] : ov;  // where the row comes from
