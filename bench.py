@@ -478,7 +478,7 @@ def overlap_compute_leg(hm, torch, np, sw, topk, tail0, W, K, w):
         f"together {tg:.3f} ms = {tg / max(ca, wa):.3f} x the longer")
     return {"copy_ms": ca, "hbm_work_ms": wa, "together_ms": tg, "together_over_longer": tg / max(ca, wa),
             "together_over_sum": tg / (ca + wa), "hbm_work": f"{reps} device-to-device copies of 600 MB",
-            "hbm_work_GBps": reps * 2 * src_bytes(600) / (wa / 1e3) / 1e9, "copy_workgroups": 64,
+            "hbm_work_GBps": reps * 2 * src_bytes(600) / (wa / 1e3) / 1e9, "copy_workgroups": 128, "copy_threads_per_workgroup": 64,
             "steps": n, "timing": "medians of steps timed one way each, in rotation"}
 
 

@@ -170,7 +170,8 @@ struct CommitArgs {
 struct CopyArgs {
   int32_t R, k, B, H, T, row16;
   int32_t rows;         // with a gather: selected rows per workgroup
-  int32_t workgroups;   // without a gather: workgroups of the copy (each takes every workgroups-th request)
+  int32_t workgroups;   // without a gather: the most workgroups the copy may take
+  int32_t slices;       // set by the launch: workgroups per request (> 1 only with fewer requests than workgroups)
   const int32_t* plan;  // [R][4][k]
   const int32_t* miss;  // [R]
   const v4u* host;
@@ -220,11 +221,12 @@ struct ResetArgs {
   int32_t* epoch;      // [R] change counters, advanced (nullptr: leave them)
 };
 
-// copy_kernel: 16-byte host loads each thread keeps in flight, and the default number of workgroups (a
-// measured point where the host link is already saturated, leaving most compute units to other work)
+// copy_kernel: 16-byte host loads each thread keeps in flight, threads per workgroup (one wave) and the number
+// of workgroups (measured: 128 one-wave workgroups hold the host link's rate within 2 % of the best grid, and
+// disturb HBM-bound work on other streams far less than fewer, larger workgroups with as many loads in flight)
 constexpr int kCopyUnroll = 8;
-constexpr int kCopyWorkgroups = 64;
-constexpr int kCopyThreads = 256;
+constexpr int kCopyWorkgroups = 128;
+constexpr int kCopyThreads = 64;
 
 // gather_kernel: threads per workgroup, 16-byte loads in flight per thread, and the chunks one workgroup
 // covers (its row count is the largest that fits, at least one)

@@ -1238,14 +1238,18 @@ __device__ __forceinline__ void plan_page_updates(const CopyArgs& a, int r, int 
   }
 }
 
-// Rows of a plan on a bounded grid: workgroup w copies the missed rows of requests w, w + gridDim.x, ... from
-// the pinned host pool into their victim slots, flattened over (miss, 16-byte chunk), each thread keeping
-// kCopyUnroll host loads in flight; then it applies those requests' page-table updates. About 128K loads in
-// flight over the chip saturate the host link, so a few dozen workgroups reach its rate and leave the other
-// compute units to concurrent work.
+// Rows of a plan on a bounded grid of one-wave workgroups. With at least as many requests as workgroups,
+// workgroup w takes requests w, w + gridDim.x, ...; with fewer, each request gets `slices` workgroups
+// (gridDim.x = R * slices) that share its chunks. A workgroup copies its requests' missed rows from the pinned
+// host pool into their victim slots, flattened over (miss, 16-byte chunk): each pass of the slices over a
+// request covers slices * kCopyThreads * kCopyUnroll consecutive chunks, each thread keeping kCopyUnroll host
+// loads in flight. Then it applies its share of those requests' page-table updates.
 __global__ __launch_bounds__(kCopyThreads) void copy_kernel(CopyArgs a) {
   const int row16 = a.row16;
-  for (int r = blockIdx.x; r < a.R; r += gridDim.x) {
+  const int S = a.slices, per = gridDim.x / S;  // per: workgroups per slice (the request stride)
+  const int sl = blockIdx.x / per;              // this workgroup's slice of each of its requests
+  const int span = kCopyThreads * kCopyUnroll;  // chunks one workgroup covers per pass
+  for (int r = blockIdx.x - sl * per; r < a.R; r += per) {
     const int m = a.miss[r];
     if (m <= 0 || m > a.k) continue;
     const int total = m * row16;
@@ -1254,7 +1258,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(CopyArgs a) {
     const int32_t* pslot = ptok + a.k;
     const v4u* hostr = a.host + (size_t)r * a.H * row16;
     v4u* hotr = a.hot + (size_t)r * a.B * row16;
-    for (int c0 = threadIdx.x; c0 < total; c0 += kCopyThreads * kCopyUnroll) {
+    for (int c0 = sl * span + threadIdx.x; c0 < total; c0 += S * span) {
       v4u v[kCopyUnroll];
       int64_t dst[kCopyUnroll];
 #pragma unroll
@@ -1274,7 +1278,7 @@ __global__ __launch_bounds__(kCopyThreads) void copy_kernel(CopyArgs a) {
       for (int u = 0; u < kCopyUnroll; ++u)
         if (dst[u] >= 0) hotr[dst[u]] = v[u];
     }
-    plan_page_updates(a, r, m, threadIdx.x, kCopyThreads);
+    plan_page_updates(a, r, m, sl * kCopyThreads + threadIdx.x, S * kCopyThreads);
   }
 }
 
@@ -1609,8 +1613,14 @@ hipError_t launch_copy(const CopyArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(copy_gather_kernel, dim3(bx, (unsigned)a.R), dim3(kGatherThreads), 0, s, a);
     return hipGetLastError();
   }
-  const int g = a.workgroups < 1 ? 1 : a.workgroups > a.R ? a.R : a.workgroups;
-  hipLaunchKernelGGL(copy_kernel, dim3(g), dim3(kCopyThreads), 0, s, a);
+  if (a.R < 1) return hipSuccess;
+  // every request the same number of workgroups: slices per request with fewer requests than workgroups,
+  // else one workgroup per request up to the bound
+  const int wg = a.workgroups < 1 ? 1 : a.workgroups;
+  CopyArgs b = a;
+  b.slices = a.R < wg ? wg / a.R : 1;
+  const int g = a.R < wg ? a.R * b.slices : wg;
+  hipLaunchKernelGGL(copy_kernel, dim3(g), dim3(kCopyThreads), 0, s, b);
   return hipGetLastError();
 }
 

@@ -206,9 +206,9 @@ int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32
  * hs_copy then moves the rows and publishes the step in the page table: each missed row is copied from the
  * host pool into its slot, the evicted tokens' page entries become -1 and the missed tokens' entries their
  * slots (the page table is not read on the decode path, so its scattered updates ride with the link-bound
- * copy instead of the plan). Without d_gather the copy runs on a bounded grid of 64 workgroups, which holds the
- * host link's rate and leaves most compute units to work on other streams. With d_gather (nullable, [R][k][row_bytes], 16-byte aligned) it also writes
- * every selected row there, as hs_resolve's fused gather does, in workgroups spread over the whole chip (the
+ * copy instead of the plan). Without d_gather the copy runs on a bounded grid of 128 one-wave workgroups,
+ * which holds the host link's rate and leaves the compute units to work on other streams. With d_gather
+ * (nullable, [R][k][row_bytes], 16-byte aligned) it also writes every selected row there, as hs_resolve's fused gather does, in workgroups spread over the whole chip (the
  * missed rows straight from the host pool); that needs a plan made with HS_PLAN_ROW_SOURCES (other plans give
  * undefined rows, never an access out of bounds). Until hs_copy completes, the hot rows of this step's new
  * slots are stale and the page table does not show the step. Two plans may run back to back, but the copy of
