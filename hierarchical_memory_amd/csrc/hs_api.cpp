@@ -88,10 +88,10 @@ int check_config(const hs_config* cfg, int32_t* H_out, hs::Layout* L_out) {
     return fail(HS_E_INVALID, "the host pool (%d requests x %lld rows x %d bytes) exceeds 2^56 bytes",
                 cfg->num_requests, (long long)H, cfg->row_bytes);
   // one workgroup's LDS: each kind of launch (with and without a gather output) takes the direct layout where
-  // it fits and the rank layout otherwise; 1 KiB of the 160 KiB of a gfx950 compute unit stays for the kernels'
-  // static LDS
+  // it fits and the rank layout otherwise (its flat bitmaps, or past their LDS the two-level ones); 1 KiB of
+  // the 160 KiB of a gfx950 compute unit stays for the kernels' static LDS
   const int k = cfg->top_k, B = cfg->device_buffer_size, T = cfg->tail_tokens;
-  const hs::Layout L = hs::make_layout(k, B, (int)H);
+  const hs::Layout L = hs::rank_layout(k, B, (int)H, hs::kLdsCap);
   const uint32_t need = std::max(hs::launch_layout(k, B, (int)H, T, false, hs::kLdsCap).total,
                                  hs::launch_layout(k, B, (int)H, T, true, hs::kLdsCap).total);
   if (need > hs::kLdsCap)
@@ -127,6 +127,7 @@ void fill_sizes(const hs_config* cfg, int32_t H, const hs::Layout& L, hs_sizes* 
   const hs::Layout lp = hs::launch_layout(kk, BB, (int)H, TT, false, hs::kLdsCap);
   const hs::Layout lg = hs::launch_layout(kk, BB, (int)H, TT, true, hs::kLdsCap);
   s->lds_bytes_rank = L.total;
+  s->sparse_rank = L.sparse;
   uint64_t tables = 0, rows = 0;
   for (const uint64_t b : {s->slot_tok_bytes, s->stamp_bytes, s->lru_order_bytes, s->page_bytes, s->step_bytes})
     tables += (b + 255) & ~255ull;
@@ -220,7 +221,7 @@ int hs_create(const hs_config* cfg, hs_ctx** out) {
   if (!ctx) return fail(HS_E_NOMEM, "out of host memory for the context");
   ctx->cfg = *cfg;
   ctx->H = H;
-  ctx->layout = L;
+  ctx->layout = hs::rank_layout(cfg->top_k, cfg->device_buffer_size, (int)H, cap);
   ctx->layout_plain = lp;
   ctx->layout_gather = lg;
   ctx->layout_plain_direct = lp;

@@ -24,6 +24,12 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));  // one 16-byte ch
 // the rank -> first position table holds the victim list from phase 4 on, the per-position ranks hold the
 // missed ids from phase 5 on, and the prefix counts of the selected set become those of the misses.
 //
+// Sparse rank layout (resolve_kernel's two-level form, for contexts whose bitmaps over token ids do not fit):
+// the same ranks, over a compact id space. A coarse bitmap marks the 32-token words that hold a selected id;
+// its prefix counts number those words 0, 1, ... (at most one per selected id), and a selected id x becomes
+// 32 * (number of x's word) + (x mod 32), which keeps the ids' order. The rank layout's bitmaps then run over
+// at most k words, and the device tail's ids have a bitmap of their own over the same compact words.
+//
 // Direct layout (resolve_direct_kernel, where it fits): a uint16 token -> slot table with one entry per host
 // row, never cleared. Each slot writes its index under its token; an id x then hits slot s = t2s[x] exactly
 // when s < B and the slot table holds x at s, so garbage left in the table by earlier work is harmless. Only
@@ -36,10 +42,12 @@ struct Layout {
   uint32_t stok, sflag, sel, selpre, first, mpre, vict, mtok, gsrc, misc;
   // direct layout
   uint32_t mbits, rbits, t2s;
-  uint32_t bm_end;  // rank layout: end of the two bitmaps (sel, hbits are adjacent and cleared together)
+  uint32_t bm_end;  // rank layout: end of the bitmaps (adjacent from sel on, cleared together)
   uint32_t direct;  // 1: direct layout
-  uint32_t words;   // bitmap words = ceil(H / 32)
+  uint32_t words;   // bitmap words = ceil(H / 32); sparse: the most compact words, min(k, ceil(H / 32))
   uint32_t total;
+  // sparse rank layout: the coarse bitmap over 32-token words and its uint16 prefix counts
+  uint32_t sparse, coarse, cpre, cwords;
 };
 
 inline uint32_t align16(uint64_t x) { return (uint32_t)((x + 15) & ~uint64_t(15)); }
@@ -75,6 +83,48 @@ inline Layout make_layout(int k, int B, int H) {
   else L.mtok = L.rank_slot;
   L.total = (uint32_t)off;
   return L;
+}
+
+// The sparse rank layout for k, B, H: the rank layout's arrays with bitmaps over at most min(k, ceil(H / 32))
+// compact words, a bitmap of the resident ids over the same words, and the coarse bitmap (one bit per 32 host
+// rows) with its prefix counts.
+inline Layout make_sparse_layout(int k, int B, int H) {
+  Layout L{};
+  const uint64_t W = ((uint64_t)H + 31) / 32;
+  L.words = (uint32_t)(W < (uint64_t)k ? W : (uint64_t)k);
+  L.cwords = (uint32_t)((W + 31) / 32);
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) { uint32_t o = (uint32_t)off; off = align16(off + bytes); return o; };
+  L.ids = take(4ull * k);
+  L.cls = take(1ull * k);
+  L.rank_slot = take(4ull * k);
+  L.rank = take(4ull * k);
+  L.stok = take(4ull * B);
+  L.ord = take(2ull * B);
+  L.sflag = take(1ull * B);
+  L.sel = take(4ull * L.words);
+  L.hbits = take(4ull * L.words);
+  L.rbits = take(4ull * L.words);
+  L.coarse = take(4ull * L.cwords);
+  L.bm_end = (uint32_t)off;
+  L.cpre = take(2ull * L.cwords);
+  L.selpre = take(2ull * L.words);
+  L.first = take(4ull * k);
+  L.mpre = L.selpre;
+  L.vict = L.first;
+  L.gsrc = take(4ull * k);
+  L.misc = take(4ull * kMiscWords);
+  if (align16(off + 4ull * k) <= kLdsCap) L.mtok = take(4ull * k);
+  else L.mtok = L.rank_slot;
+  L.total = (uint32_t)(off > 0xffffffffull ? 0xffffffffull : off);
+  L.sparse = 1;
+  return L;
+}
+
+// The rank layout a context of this shape takes: the flat one where it fits in cap, else the sparse one.
+inline Layout rank_layout(int k, int B, int H, uint64_t cap) {
+  const Layout F = make_layout(k, B, H);
+  return F.total <= cap ? F : make_sparse_layout(k, B, H);
 }
 
 // Ids and slots per thread of the direct kernel: (2, 4) for k <= 2048 and B <= 4096, else (8, 8); it holds at
@@ -113,10 +163,10 @@ inline Layout make_direct_layout(int k, int B, int H, int T, bool gather, uint64
   return L;
 }
 
-// The layout a launch takes: the direct one where it fits, else the rank one.
+// The layout a launch takes: the direct one where it fits, else the rank one (flat, or sparse beyond it).
 inline Layout launch_layout(int k, int B, int H, int T, bool gather, uint64_t cap) {
   const Layout D = make_direct_layout(k, B, H, T, gather, cap);
-  return D.direct ? D : make_layout(k, B, H);
+  return D.direct ? D : rank_layout(k, B, H, cap);
 }
 
 struct ResolveArgs {

@@ -266,7 +266,9 @@ __device__ __forceinline__ void rows_phase(const ResolveArgs& a, int r, int m, c
 //           evicted token and position) and gather every selected row, the missed ones straight from the
 //           host pool; commit_kernel applies accepted records later (hs_trial / hs_commit).
 // kFifo: FIFO replacement instead of LRU (hits keep their stamps and their place in the order list).
-template <int kMode, bool kFifo>
+// kSparse: the two-level bitmaps of the sparse rank layout (contexts past the flat bitmaps' LDS): every bitmap
+// below runs over compact words, word number vw(x) for a selected id x, the same bit x mod 32 within it.
+template <int kMode, bool kFifo, bool kSparse>
 __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const Layout& L = a.L;
@@ -294,10 +296,22 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
                             ? reinterpret_cast<uint16_t*>(a.trial + (size_t)r * a.trial_words + kTrialHead + 4 * a.k)
                             : a.order + (size_t)r * a.B;
   const int k = a.k, B = a.B, H = a.H, T = a.T;
-  const int W = (int)L.words;
+  int W = (int)L.words;  // sparse: the compact words in use, known once the coarse bitmap is counted
   const bool has_tail = a.tail0 != nullptr;
   constexpr bool fifo = kFifo;
   const int32_t t0 = has_tail ? a.tail0[r] : 0;
+  uint32_t* coarse = (uint32_t*)(smem + L.coarse);  // sparse: one bit per 32-token word holding a selected id
+  uint16_t* cpre = (uint16_t*)(smem + L.cpre);      // sparse: compact words before each coarse word
+  uint32_t* rbits = (uint32_t*)(smem + L.rbits);    // sparse: resident ids, over the compact words
+  // the bitmap word of a selected id: its 32-token word, or in the sparse layout that word's compact number
+  auto vw = [&](int32_t x) -> int {
+    if constexpr (kSparse) {
+      const int c_ = x >> 10;
+      return (int)cpre[c_] + __popc(coarse[c_] & ((1u << ((x >> 5) & 31)) - 1u));
+    } else {
+      return x >> 5;
+    }
+  };
   const int32_t t = a.step[r];
   const size_t rk = (size_t)r * k, rB = (size_t)r * B, rH = (size_t)r * H;
   // per-request bases (uniform): with at(), stores take the scalar-base form with no 64-bit address arithmetic
@@ -309,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   int32_t* const plan_r = a.plan + 4 * rk;  // used by plan launches only
   const bool sources = kMode == kPlan && a.plan_sources != 0;
   // thread-contiguous chunks of bitmap words and of slots / order positions
-  const int cw = (W + kThreads - 1) / kThreads, w0 = min(W, tid * cw), w1 = min(W, w0 + cw);
+  int cw = (W + kThreads - 1) / kThreads, w0 = min(W, tid * cw), w1 = min(W, w0 + cw);
   const int cb = (B + kThreads - 1) / kThreads, s0 = min(B, tid * cb), s1 = min(B, s0 + cb);
   // x - t0 is exact in uint32 once x >= t0, whatever the signs
   auto resident = [&](int32_t x) { return has_tail && x >= t0 && (uint32_t)x - (uint32_t)t0 < (uint32_t)T; };
@@ -320,7 +334,10 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   // words that the window touches at all (uniform); elsewhere the mask is zero and is not computed
   const int win_w0 = win_lo >> 5, win_w1 = win_hi > win_lo ? (win_hi - 1) >> 5 : -1;
   auto wmask = [&](int w) { return (w >= win_w0 && w <= win_w1) ? window_bits(w, win_lo, win_hi) : 0u; };
-  auto cand_word = [&](int w) { return has_tail ? sel[w] & ~wmask(w) : sel[w]; };
+  auto cand_word = [&](int w) {
+    if constexpr (kSparse) return sel[w] & ~rbits[w];
+    else return has_tail ? sel[w] & ~wmask(w) : sel[w];
+  };
   int st = 0;
 
   // ---- phase 0: stage and classify, and build the bitmap of selected ids. The first round of every global
@@ -370,10 +387,14 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   // selection repeats an id. Without branches: an id that is not selected ORs nothing into word 0.
   auto mark = [&](int32_t x, int8_t c) {
     const bool s = c == C_CAND || c == C_RES;
-    const int wi = s ? (x >> 5) : 0;
-    const uint32_t bit = s ? 1u << (x & 31) : 0u;
-    const uint32_t old = atomicOr(&sel[wi], bit);
-    repeat |= (old & bit) != 0u;
+    if constexpr (kSparse) {  // the coarse bit of x's word; the id's own bit waits for the compact numbering
+      atomicOr(&coarse[s ? (x >> 10) : 0], s ? 1u << ((x >> 5) & 31) : 0u);
+    } else {
+      const int wi = s ? (x >> 5) : 0;
+      const uint32_t bit = s ? 1u << (x & 31) : 0u;
+      const uint32_t old = atomicOr(&sel[wi], bit);
+      repeat |= (old & bit) != 0u;
+    }
   };
   auto ids4 = [&](int i, int4 x) {
     reinterpret_cast<int4*>(ids)[i] = x;
@@ -386,18 +407,21 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     for (int u = 0; u < 4; ++u) {
       c[u] = classify(xs[u]);
       const bool s = c[u] == C_CAND || c[u] == C_RES;
-      wi[u] = s ? (xs[u] >> 5) : 0;
-      bit[u] = s ? 1u << (xs[u] & 31) : 0u;
+      wi[u] = s ? (kSparse ? (xs[u] >> 10) : (xs[u] >> 5)) : 0;
+      bit[u] = s ? 1u << (kSparse ? ((xs[u] >> 5) & 31) : (xs[u] & 31)) : 0u;
     }
     reinterpret_cast<uint32_t*>(cls)[i] = (uint32_t)(uint8_t)c[0] | ((uint32_t)(uint8_t)c[1] << 8) |
                                           ((uint32_t)(uint8_t)c[2] << 16) | ((uint32_t)(uint8_t)c[3] << 24);
     // what mark does, for four ids at once: every atomic is issued before the first result is looked at
+    uint32_t* const bm = kSparse ? coarse : sel;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) old[u] = atomicOr(&sel[wi[u]], bit[u]);
-    uint32_t rep = 0u;
+    for (int u = 0; u < 4; ++u) old[u] = atomicOr(&bm[wi[u]], bit[u]);
+    if constexpr (!kSparse) {
+      uint32_t rep = 0u;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) rep |= old[u] & bit[u];
-    repeat |= rep != 0u;
+      for (int u = 0; u < 4; ++u) rep |= old[u] & bit[u];
+      repeat |= rep != 0u;
+    }
   };
 
   if (tid < n4B) stage4(tid, y0, o0);
@@ -422,6 +446,37 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       cls[i] = c;
       rank_slot[i] = -1;
       mark(x, c);
+    }
+  }
+  if constexpr (kSparse) {
+    // number the marked 32-token words in id order (a block scan of the coarse words' popcounts), then put
+    // each selected id into the bitmaps over its compact word; finding its bit set means a repeated id
+    __syncthreads();
+    const int CW = (int)L.cwords;
+    const int ccw = (CW + kThreads - 1) / kThreads, c0 = min(CW, tid * ccw), c1 = min(CW, c0 + ccw);
+    int cnt = 0;
+    for (int w = c0; w < c1; ++w) cnt += __popc(coarse[w]);
+    int n_words;
+    int run = block_excl_scan(cnt, misc + kMiscScanSel, lane, wave, &n_words);
+    for (int w = c0; w < c1; ++w) {
+      cpre[w] = (uint16_t)run;
+      run += __popc(coarse[w]);
+    }
+    W = min(n_words, (int)L.words);  // n_words <= k: every marked word holds a selected id
+    cw = (W + kThreads - 1) / kThreads;
+    w0 = min(W, tid * cw);
+    w1 = min(W, w0 + cw);
+    __syncthreads();
+    for (int i = tid; i < k; i += kThreads) {
+      const int8_t c = cls[i];
+      if (c == C_CAND || c == C_RES) {
+        const int32_t x = ids[i];
+        const int v = vw(x);
+        const uint32_t bit = 1u << (x & 31);
+        const uint32_t old = atomicOr(&sel[v], bit);
+        repeat |= (old & bit) != 0u;
+        if (c == C_RES) atomicOr(&rbits[v], bit);
+      }
     }
   }
   // one barrier publishes both flags (every writer stores the same 1)
@@ -493,18 +548,24 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     const int8_t c = cls[i];
     if (c == C_CAND || c == C_RES) {
       const int32_t x = ids[i];
-      const int q = (int)selpre[x >> 5] + __popc(sel[x >> 5] & below(x));
+      const int v = vw(x);
+      const int q = (int)selpre[v] + __popc(sel[v] & below(x));
       rnk[i] = q;
       if (repeats) atomicMin(&first[q], i);
     }
   }
   auto probe_slot = [&](int s, int32_t y) {
     if (y < 0 || resident(y)) return;  // empty, or resident (a resident id takes no slot)
-    const uint32_t word = sel[y >> 5];
+    int v = y >> 5;
+    if constexpr (kSparse) {  // no selected id in y's 32-token word: not selected
+      if (!(coarse[y >> 10] & (1u << ((y >> 5) & 31)))) return;
+      v = vw(y);
+    }
+    const uint32_t word = sel[v];
     if (word & (1u << (y & 31))) {
-      rank_slot[(int)selpre[y >> 5] + __popc(word & below(y))] = s;
+      rank_slot[(int)selpre[v] + __popc(word & below(y))] = s;
       sflag[s] = 1;
-      atomicOr(&hbits[y >> 5], 1u << (y & 31));
+      atomicOr(&hbits[v], 1u << (y & 31));
     }
   };
   if (whole4) {
@@ -547,10 +608,19 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
       uint32_t hw[4];
       load_words(sel, mw);
       load_words(hbits, hw);
-      const bool touched = has_tail && w0 + cw > win_w0 && w0 <= win_w1;
+      if constexpr (kSparse) {
+        uint32_t rw[4];
+        load_words(rbits, rw);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mw[u] &= ~rw[u];
+      } else {
+        const bool touched = has_tail && w0 + cw > win_w0 && w0 <= win_w1;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (touched) mw[u] &= ~window_bits(w0 + u, win_lo, win_hi);
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (touched) mw[u] &= ~window_bits(w0 + u, win_lo, win_hi);
         mw[u] &= ~hw[u];
         cm += __popc(mw[u]);
       }
@@ -629,10 +699,10 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
     const int32_t x = ids[i];
     int32_t o = -1, g = -1;
     const bool cand = c == C_CAND;
-    const int w = x >> 5;
     int32_t hit = -1;
     if (cand) hit = settle ? rnk[i] : rank_slot[rnk[i]];
     if (cand && hit < 0) {  // a miss
+      const int w = vw(x);
       const uint32_t cwd = cand_word(w);
       const int j = (int)mpre[w] + __popc(cwd & ~hbits[w] & below(x));
       const int v = vict[j];
@@ -1561,9 +1631,12 @@ hipError_t launch_rebuild_order(const RebuildArgs& a, hipStream_t s) {
 
 hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes) {
   const void* resolve_variants[] = {
-      (const void*)resolve_kernel<kFused, false>, (const void*)resolve_kernel<kFused, true>,
-      (const void*)resolve_kernel<kPlan, false>,  (const void*)resolve_kernel<kPlan, true>,
-      (const void*)resolve_kernel<kTrial, false>, (const void*)resolve_kernel<kTrial, true>,
+      (const void*)resolve_kernel<kFused, false, false>, (const void*)resolve_kernel<kFused, true, false>,
+      (const void*)resolve_kernel<kPlan, false, false>,  (const void*)resolve_kernel<kPlan, true, false>,
+      (const void*)resolve_kernel<kTrial, false, false>, (const void*)resolve_kernel<kTrial, true, false>,
+      (const void*)resolve_kernel<kFused, false, true>, (const void*)resolve_kernel<kFused, true, true>,
+      (const void*)resolve_kernel<kPlan, false, true>,  (const void*)resolve_kernel<kPlan, true, true>,
+      (const void*)resolve_kernel<kTrial, false, true>, (const void*)resolve_kernel<kTrial, true, true>,
       (const void*)resolve_direct_kernel<kFused, false, 2, 4>, (const void*)resolve_direct_kernel<kFused, true, 2, 4>,
       (const void*)resolve_direct_kernel<kPlan, false, 2, 4>,  (const void*)resolve_direct_kernel<kPlan, true, 2, 4>,
       (const void*)resolve_direct_kernel<kTrial, false, 2, 4>, (const void*)resolve_direct_kernel<kTrial, true, 2, 4>,
@@ -1585,7 +1658,9 @@ hipError_t set_lds_limits(uint32_t resolve_bytes, uint32_t rebuild_bytes) {
 template <int kMode, bool kFifo>
 static void launch_mode_policy(const ResolveArgs& a, hipStream_t s) {
   const dim3 grid(a.R), block(kThreads);
-  if (!a.L.direct) hipLaunchKernelGGL((resolve_kernel<kMode, kFifo>), grid, block, a.L.total, s, a);
+  if (!a.L.direct && a.L.sparse)
+    hipLaunchKernelGGL((resolve_kernel<kMode, kFifo, true>), grid, block, a.L.total, s, a);
+  else if (!a.L.direct) hipLaunchKernelGGL((resolve_kernel<kMode, kFifo, false>), grid, block, a.L.total, s, a);
   else if (a.k <= 2 * kThreads && a.B <= 4 * kThreads)
     hipLaunchKernelGGL((resolve_direct_kernel<kMode, kFifo, 2, 4>), grid, block, a.L.total, s, a);
   else hipLaunchKernelGGL((resolve_direct_kernel<kMode, kFifo, 8, 8>), grid, block, a.L.total, s, a);

@@ -53,7 +53,7 @@ class HsSizes(ctypes.Structure):
                 ("plan_bytes", ctypes.c_uint64), ("trial_bytes", ctypes.c_uint64), ("lds_bytes", ctypes.c_uint32),
                 ("lds_bytes_launch", ctypes.c_uint32), ("lds_bytes_launch_gather", ctypes.c_uint32),
                 ("token_slot_table", ctypes.c_uint32), ("lds_bytes_rank", ctypes.c_uint32),
-                ("epoch_bytes", ctypes.c_uint64), ("state_tables_bytes", ctypes.c_uint64),
+                ("sparse_rank", ctypes.c_uint32), ("epoch_bytes", ctypes.c_uint64), ("state_tables_bytes", ctypes.c_uint64),
                 ("state_rows_bytes", ctypes.c_uint64)]
 
 

@@ -81,7 +81,12 @@ extern "C" {
  * Elsewhere it ranks the selected ids in bitmaps over token ids (the rank
  * layout: about 21k + 7B + 10 * ceil(H / 32) bytes, plus 4k more where that
  * still fits, which saves the kernel a pass; at k = 2048 and B = 4096 that
- * allows about 290,000 host rows). hs_sizes reports the bytes of each.
+ * allows about 290,000 host rows). Past that the same ranks run over compact
+ * ids: a coarse bitmap with one bit per 32 host rows numbers the 32-row words
+ * that hold a selected id, and the bitmaps cover only those words (the sparse
+ * rank layout: about 39k + 7B + 6 * ceil(H / 1024) bytes; at k = 2048 and
+ * B = 4096 up to about 10.5 million host rows). hs_sizes reports the bytes of
+ * each and which rank layout the shape takes.
  */
 typedef struct hs_config {
   int32_t num_requests;       /* R, 1 .. 65535 */
@@ -144,6 +149,8 @@ typedef struct hs_sizes {
   uint32_t token_slot_table;        /* bit 0: launches without a gather output use the direct layout;
                                        bit 1: launches with one do */
   uint32_t lds_bytes_rank;          /* LDS of the rank layout of this shape (whether or not launches take it) */
+  uint32_t sparse_rank;             /* 1: that rank layout is the two-level one (contexts past the flat
+                                       bitmaps' LDS) */
   uint64_t epoch_bytes;             /* [R] int32 change counters */
   uint64_t state_tables_bytes;      /* snapshot of the tables (HS_STATE_TABLES), see hs_export_state */
   uint64_t state_rows_bytes;        /* snapshot of the hot and tail rows (HS_STATE_ROWS) */

@@ -121,19 +121,32 @@ def test_lds_layout_takes_the_missed_token_array_where_it_fits():
         assert lds(k, B, H) + 4 * k > 159 * 1024
 
 
-def test_context_length_limit_of_the_rank_layout():
-    """At k = 2048 and B = 4096 the rank layout holds about 290,000 host rows per request (262,144 is accepted);
-    past 159 KiB the shape is refused."""
-    ok = hm.hs_required_sizes(hm.config(2, 2048, 4096, 0.0, 64, 262144))
-    assert ok.lds_bytes <= 159 * 1024 and ok.token_slot_table == 0
+def test_context_length_limits_of_the_rank_layouts():
+    """At k = 2048 and B = 4096 the flat rank layout holds about 290,000 host rows per request (262,144 take
+    it). Past that the two-level layout takes over: its bitmaps run over at most k compact words, plus a coarse
+    bitmap of one bit per 32 host rows and its uint16 prefix counts, up to about 10.5 million host rows; past
+    159 KiB the shape is refused."""
+    def req(H):
+        return hm.hs_required_sizes(hm.config(2, 2048, 4096, 0.0, 64, H))
+    ok = req(262144)
+    assert ok.lds_bytes <= 159 * 1024 and ok.token_slot_table == 0 and ok.sparse_rank == 0
     limit = 159 * 1024 - (21 * 2048 + 7 * 4096 + MISC)
     h_max = (limit // 10) * 32
     assert 280000 < h_max < 300000
-    hm.hs_required_sizes(hm.config(2, 2048, 4096, 0.0, 64, h_max - 4096))
-    for H in (h_max + 32 * 64, 1 << 20):
-        with pytest.raises(hm.HiSparseError) as err:
-            hm.hs_required_sizes(hm.config(2, 2048, 4096, 0.0, 64, H))
-        assert err.value.code == hm.HS_E_INVALID and "LDS" in str(err.value)
+    assert req(h_max - 4096).sparse_rank == 0
+    for H in (h_max + 32 * 64, 1 << 20, 3_000_000):
+        s = req(H)
+        wc = -(-H // 1024)  # coarse words
+        base = 39 * 2048 + 7 * 4096 + 6 * wc + MISC
+        assert s.sparse_rank == 1 and s.token_slot_table == 0
+        assert 0 <= s.lds_bytes - base <= 256 and s.lds_bytes <= 159 * 1024, (H, s.lds_bytes, base)
+    # near the limit the missed tokens share the rank -> slot table (4k bytes fewer)
+    wc_max = (159 * 1024 - (35 * 2048 + 7 * 4096 + MISC)) // 6
+    assert 10_000_000 < wc_max * 1024 < 11_000_000
+    assert req(wc_max * 1024 - 64 * 1024).sparse_rank == 1
+    with pytest.raises(hm.HiSparseError) as err:
+        req(wc_max * 1024 + 64 * 1024)
+    assert err.value.code == hm.HS_E_INVALID and "LDS" in str(err.value)
 
 
 def test_binding_refuses_host_tensors():

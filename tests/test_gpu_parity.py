@@ -150,6 +150,78 @@ def test_context_of_262144_tokens():
     p.close()
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shapes_sparse_layout(seed):
+    """Contexts of 600,000 to 1,200,000 tokens with small k and B: past the flat bitmaps' LDS, so every launch
+    takes the two-level rank layout. Most ids come from a window of about 3B tokens (slots are hit), the rest
+    from the whole context (many 32-token words, most holding one id); padding, bad and repeated ids, a device
+    tail on some seeds, FIFO on others, with and without the gather."""
+    import hierarchical_memory_amd as hm
+    rng = np.random.default_rng(30_000 + seed)
+    k = int(rng.integers(1, 300))
+    B = int(rng.integers(k, 3 * k + 2))
+    H = int(rng.integers(600_000, 1_200_000))
+    T = int(rng.integers(1, 64)) if seed % 3 == 0 else 0
+    rb = int(rng.choice([16, 32]))
+    R = int(rng.integers(1, 5))
+    policy, gather, steps = seed % 2, bool(seed % 4 < 2), 6
+    sizes = hm.hs_required_sizes(hm.config(R, k, B, 0.0, rb, H, T, policy))
+    assert sizes.token_slot_table == 0 and sizes.sparse_rank == 1
+    lo = int(rng.integers(0, H - 3 * B - 8))
+    ids = np.empty((R, steps, k), np.int32)
+    for r in range(R):
+        for t in range(steps):
+            near = (lo + rng.choice(3 * B, size=k, replace=False)).astype(np.int32)
+            far = rng.integers(0, H, size=k).astype(np.int32)
+            row = np.where(rng.random(k) < 0.7, near, far)
+            weird = rng.random(k) < 0.05
+            row[weird] = rng.integers(-3, H + 3, size=int(weird.sum()))
+            ids[r, t] = row
+    log(f"[sparse shape {seed}] R={R} k={k} B={B} H={H} T={T} rb={rb} policy={policy} gather={gather}")
+    w = workload.SINGLE_4K.with_(name=f"sparse_{seed}", num_requests=R, top_k=k, buffer_slots=B, host_rows=H, L0=H,
+                                 tail_tokens=T, row_elems=rb // 2, steps=steps, fused_gather=gather)
+    tail0 = (lo + rng.integers(0, 3 * B, size=R)).astype(np.int32) if T else None
+    p = Pair(w, ids=ids, tail0=tail0, gather=gather, policy=policy)
+    p.run(check_every=1)
+    p.close()
+
+
+@pytest.mark.parametrize("tail", [0, 8192])
+def test_context_of_one_million_tokens(tail):
+    """A 1,048,576-token context at k = 2048, B = 4096 (the two-level rank layout), with and without a device
+    tail of 8192 tokens at its end: fused resolve with a gather, then plan + copy, step by step against the
+    oracle, with a repeated id on odd steps."""
+    import hierarchical_memory_amd as hm
+    H = 1 << 20
+    w = workload.SINGLE_4K.with_(name=f"context_1M_T{tail}", num_requests=2, top_k=2048, buffer_slots=4096,
+                                 host_rows=H, L0=H, window=12000, row_elems=32, steps=8, fused_gather=True,
+                                 tail_tokens=tail)
+    sizes = hm.hs_required_sizes(hm.config(2, 2048, 4096, 0.0, 64, H, tail))
+    assert sizes.token_slot_table == 0 and sizes.sparse_rank == 1 and sizes.lds_bytes <= 159 * 1024
+    ids = workload.streams(w)
+    ids[:, 1::2, 9] = ids[:, 1::2, 4]
+    tail0 = np.full(2, H - tail, np.int32) if tail else None
+    log(f"[1M context] tail {tail}: fused with gather")
+    p = Pair(w, ids=ids, tail0=tail0, gather=True)
+    p.run(check_every=1)
+    p.close()
+    log(f"[1M context] tail {tail}: plan + copy")
+    p = Pair(w, ids=ids, tail0=tail0)
+    plan = p.sw.plan_buffer()
+    out, miss, status, _ = p.outs
+    for t in range(w.steps):
+        step_ids = p.ids[:, t]
+        hm.hs_plan(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(step_ids)).cuda(), p.tail0_dev, out, miss,
+                   status, plan)
+        hm.hs_copy(p.sw.ctx, plan, miss)
+        o_out, o_miss, o_status, _ = p.o.step(step_ids[p.sample], None if tail0 is None else tail0[p.sample])
+        assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+        assert (status.cpu().numpy() == o_status).all()
+        p.t += 1
+        p.check_state()
+    p.close()
+
+
 def test_single_request_full():
     p = Pair(workload.SINGLE_4K, gather=True)
     p.run(check_every=1)
