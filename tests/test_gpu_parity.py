@@ -220,6 +220,22 @@ def test_context_of_one_million_tokens(tail):
         p.t += 1
         p.check_state()
     p.close()
+    log(f"[1M context] tail {tail}: trial + commit")
+    p = Pair(w, ids=ids, tail0=tail0, gather=True)
+    trial = p.sw.trial_buffer()
+    out, miss, status, g = p.outs
+    for t in range(4):
+        step_ids = p.ids[:, t]
+        hm.hs_trial(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(step_ids)).cuda(), p.tail0_dev, out, miss,
+                    status, g, trial)
+        o_out, o_miss, o_status, o_g = p.o.step(step_ids[p.sample], None if tail0 is None else tail0[p.sample],
+                                                gather=True)
+        assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+        assert (g.cpu().numpy() == o_g).all()
+        hm.hs_commit(p.sw.ctx, trial, g)
+        p.t += 1
+        p.check_state()
+    p.close()
 
 
 def test_single_request_full():
