@@ -149,7 +149,8 @@ inline Layout make_direct_layout(int k, int B, int H, int T, bool gather, uint64
   L.mtok = take(4ull * k);
   L.gsrc = gather ? take(4ull * k) : 0u;
   L.misc = take(4ull * kMiscWords);
-  // the table's region, holding the repeat path's arrays once the table is dead
+  // the table's region, holding the repeat path's arrays once the table is dead, then a plan launch's
+  // evicted tokens and the staged new order
   const uint64_t region = off;
   L.t2s = (uint32_t)region;
   L.sel = take(4ull * L.words);
@@ -157,6 +158,9 @@ inline Layout make_direct_layout(int k, int B, int H, int T, bool gather, uint64
   L.first = take(4ull * k);
   const uint64_t table = align16(2ull * (uint64_t)H + 2);
   if (off < region + table) off = region + table;
+  // the region also takes, once the table is dead, a plan's evicted tokens (4k) and the staged new order (2B)
+  const uint64_t staged = align16(4ull * k) + 2ull * B;
+  if (off < region + staged) off = region + staged;
   L.total = (uint32_t)off;
   const bool bitmaps_ok = L.words <= 3u * kThreads && (L.mpre - L.mbits) <= 2u * 16u * kThreads;
   L.direct = (off <= cap && B <= kDirectMaxSlots && B % 4 == 0 && bitmaps_ok) ? 1u : 0u;

@@ -18,7 +18,8 @@
 //   D  j-th missed id -> j-th victim: page table, slot table, stamps, outputs; a second scan closes the new
 //      order with the slots used this step, in slot order;
 //   E  the missed rows are copied from mapped pinned host memory (and every selected row gathered when fused).
-// Ids and order entries stay in registers from A to D; there are five barriers.
+// Ids and order entries stay in registers from A to D; the new order is staged in LDS and written at the end in
+// one 8-byte store per thread; there are six barriers.
 //
 // resolve_kernel (every shape, the rank layout):
 //   phase 0  the same loads, staged in LDS; ids classified and put into a bitmap of selected ids;
@@ -822,8 +823,16 @@ __device__ __forceinline__ void st16(uint32_t v, rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void st32(uint32_t v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kStream);
 }
+// the same with a uniform byte offset added to the lane's (valid lane offsets stay inside the buffer with it;
+// kNoAccess plus it stays past the end)
+__device__ __forceinline__ void st32_at(uint32_t v, rsrc_t r, uint32_t off, uint32_t uniform_off) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, (int)uniform_off, kStream);
+}
 __device__ __forceinline__ void st32_scattered(uint32_t v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void st64(v2u v, rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)off, 0, kStream);
 }
 __device__ __forceinline__ void st128(v4u v, rsrc_t r, uint32_t off) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStream);
@@ -850,6 +859,10 @@ __global__ __launch_bounds__(kThreads) void resolve_direct_kernel(ResolveArgs a)
   int32_t* gsrc = (int32_t*)(smem + L.gsrc);
   int32_t* misc = (int32_t*)(smem + L.misc);
   uint16_t* t2s = (uint16_t*)(smem + L.t2s);  // token -> slot that holds it (valid only where the slot agrees)
+  // in the table's region, dead after the id tests (it holds at least 4k + 2B bytes): a plan launch's evicted
+  // tokens by victim rank, and the new LRU order, staged so that it goes out as one 8-byte store per thread
+  int32_t* evt = (int32_t*)(smem + L.t2s);
+  uint16_t* nord_l = (uint16_t*)(smem + L.t2s + ((4u * (uint32_t)a.k + 15u) & ~15u));
   // LDS addresses a lane stores to when it has nothing to store
   unsigned char* const dummy = smem + L.misc + 4 * kMiscDummy;
 
@@ -1101,18 +1114,26 @@ __global__ __launch_bounds__(kThreads) void resolve_direct_kernel(ResolveArgs a)
       if (kMode == kFused) {
         const int32_t yo = stok[isv ? slot : 0u];
         st32_scattered(0xffffffffu, page_b, (isv & (yo >= 0)) ? 4u * (uint32_t)yo : kNoAccess);
-      } else if (kMode == kPlan) {  // the miss list for the copy: the victim and the token it held
+      } else if (kMode == kPlan) {  // the token the victim held, for the plan's evicted-token list
         const int32_t yo = stok[isv ? slot : 0u];
-        st32(slot, plan_b, isv ? 4u * (uint32_t)(k + runC) : kNoAccess);
-        st32((uint32_t)yo, plan_b, isv ? 4u * (uint32_t)(2 * k + runC) : kNoAccess);
+        *reinterpret_cast<int32_t*>(isv ? (unsigned char*)(evt + runC) : dummy) = yo;
       }
       const bool keep = fifo ? (in & !isv) : (nonhit & !isv);
       const int np = fifo ? (nonhit ? p - m : p - min(m, runC)) : runC - m;
-      st16(slot, nord_b, keep ? 2u * (uint32_t)np : kNoAccess);
+      *(keep ? nord_l + np : reinterpret_cast<uint16_t*>(dummy)) = (uint16_t)slot;
       runC += nonhit ? 1 : 0;
     }
   }
   __syncthreads();  // (4)
+  if (kMode == kPlan) {
+    // the plan's victim and evicted-token lists, dense by victim rank (staged in LDS by the victim pass): only
+    // the waves holding ranks below m store anything, and the stores drain while the pairing runs
+    for (int j = tid; j < m; j += kThreads) {
+      const uint32_t jo = 4u * (uint32_t)j;
+      st32_at((uint32_t)vict[j], plan_b, jo, 4u * (uint32_t)k);
+      st32_at((uint32_t)evt[j], plan_b, jo, 8u * (uint32_t)k);
+    }
+  }
 
   // ---- D: the j-th missed id takes the j-th victim: outputs, the new tokens' page entries (fused; a plan leaves
   // them to the copy), the LDS slot table
@@ -1185,7 +1206,7 @@ __global__ __launch_bounds__(kThreads) void resolve_direct_kernel(ResolveArgs a)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const bool u = used((fw[q] >> (8 * b)) & 0xffu);
-        st16((uint32_t)(s0 + 4 * q + b), nord_b, u ? 2u * (uint32_t)pos : kNoAccess);  // pos < B for a permutation
+        *(u ? nord_l + pos : reinterpret_cast<uint16_t*>(dummy)) = (uint16_t)(s0 + 4 * q + b);
         pos += u ? 1 : 0;
       }
   }
@@ -1204,6 +1225,13 @@ __global__ __launch_bounds__(kThreads) void resolve_direct_kernel(ResolveArgs a)
       st128(ns, stamp_b, off);
       st128(*reinterpret_cast<const v4u*>(stok + (inq[q] ? s0 + 4 * q : 0)), stok_b, off);
     }
+  }
+  // the new order, complete in LDS after this barrier: this thread's four entries per chunk in one store
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    const v2u ov = *reinterpret_cast<const v2u*>(nord_l + (inq[q] ? s0 + 4 * q : 0));
+    st64(ov, nord_b, inq[q] ? 2u * (uint32_t)(s0 + 4 * q) : kNoAccess);
   }
   const int status = [&] {
     int v = lane < kWaves ? misc[kMiscWaveSt + lane] : 0;

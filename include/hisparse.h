@@ -75,9 +75,9 @@ extern "C" {
  * hs_required_sizes and hs_create return HS_E_INVALID otherwise. A launch
  * takes one of two layouts. Where a uint16 token -> slot entry for each of
  * the H host rows fits (the direct layout: about 8k + 5B + T / 8 +
- * 6 * ceil(H / 32) + max(2H, 6 * ceil(H / 32) + 4k) bytes, 4k more with a
- * gather output, and B <= 8192), it tests each selected id against the slot
- * table directly.
+ * 6 * ceil(H / 32) + max(2H, 6 * ceil(H / 32) + 4k, 4k + 2B) bytes, 4k more
+ * with a gather output, and B <= 8192), it tests each selected id against the
+ * slot table directly.
  * Elsewhere it ranks the selected ids in bitmaps over token ids (the rank
  * layout: about 21k + 7B + 10 * ceil(H / 32) bytes, plus 4k more where that
  * still fits, which saves the kernel a pass; at k = 2048 and B = 4096 that

@@ -175,8 +175,8 @@ def test_build_script_loads_without_the_built_library():
 
 def test_token_slot_table_where_it_fits():
     """Launches take the direct layout (a uint16 token -> slot entry per host row) where it fits in 159 KiB and
-    B <= 8192: about 8k + 8B + 6 ceil(H/32) + max(2H, 6 ceil(H/32) + 4k) bytes, 4k more with a gather output;
-    elsewhere the rank layout."""
+    B <= 8192: about 8k + 5B + T/8 + 6 ceil(H/32) + max(2H, 6 ceil(H/32) + 4k, 4k + 2B) bytes, 4k more with a
+    gather output; elsewhere the rank layout."""
     cap = 159 * 1024
     # (k, B, H, T, expected bits): 256-request, 32-request and single-request shapes both ways, hybrid and sweep
     # shapes neither, a buffer past the direct kernel's 8192 slots neither
@@ -188,7 +188,8 @@ def test_token_slot_table_where_it_fits():
         W = _words(H)
         for bit, got, extra in ((1, s.lds_bytes_launch, 0), (2, s.lds_bytes_launch_gather, 4 * k)):
             if bits & bit:
-                est = 8 * k + 4 * B + 4 * ((B + 3) // 4) + 6 * W + 4 * ((T + 31) // 32) + MISC + max(2 * H, 6 * W + 4 * k) + extra
+                region = max(2 * H, 6 * W + 4 * k, 4 * k + 2 * B)  # table, repeat arrays, staged lists
+                est = 8 * k + 4 * B + 4 * ((B + 3) // 4) + 6 * W + 4 * ((T + 31) // 32) + MISC + region + extra
                 assert est <= got <= est + 256 and got <= cap, (k, B, H, bit, got, est)
             else:
                 assert got == s.lds_bytes_rank, (k, B, H, bit, got, s.lds_bytes_rank)
