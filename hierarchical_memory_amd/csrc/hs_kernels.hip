@@ -1134,6 +1134,27 @@ __global__ __launch_bounds__(kThreads) void resolve_direct_kernel(ResolveArgs a)
       st32_at((uint32_t)evt[j], plan_b, jo, 8u * (uint32_t)k);
     }
   }
+  // the slots used this step (hits and victims under LRU, victims under FIFO) are final: their stamps become t,
+  // and the stamp rows go out now, to drain while the pairing runs
+  auto used = [&](uint32_t f) { return fifo ? f == 2u : f != 0u; };
+  uint32_t fw[kQ];
+#pragma unroll
+  for (int q = 0; q < kQ; ++q) {
+    fw[q] = sflagw[inq[q] ? (s0 >> 2) + q : 0];
+    fw[q] = inq[q] ? fw[q] : 0u;
+  }
+  if (kMode != kTrial) {
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const uint32_t f = fw[q];
+      v4u ns;
+      ns.x = used(f & 0xffu) ? (uint32_t)t : sq[q].x;
+      ns.y = used((f >> 8) & 0xffu) ? (uint32_t)t : sq[q].y;
+      ns.z = used((f >> 16) & 0xffu) ? (uint32_t)t : sq[q].z;
+      ns.w = used(f >> 24) ? (uint32_t)t : sq[q].w;
+      st128(ns, stamp_b, inq[q] ? 4u * (uint32_t)(s0 + 4 * q) : kNoAccess);
+    }
+  }
 
   // ---- D: the j-th missed id takes the j-th victim: outputs, the new tokens' page entries (fused; a plan leaves
   // them to the copy), the LDS slot table
@@ -1188,17 +1209,12 @@ __global__ __launch_bounds__(kThreads) void resolve_direct_kernel(ResolveArgs a)
   // the slots used this step close the new order in slot order: hits and victims (LRU) or victims only
   // (FIFO); the scan's barrier also publishes the LDS writes above
   const int tail_start = fifo ? B - m : ncand - m;
-  auto used = [&](uint32_t f) { return fifo ? f == 2u : f != 0u; };
-  uint32_t fw[kQ];
   {
     int ch = 0;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
-      fw[q] = sflagw[inq[q] ? (s0 >> 2) + q : 0];
-      fw[q] = inq[q] ? fw[q] : 0u;
+    for (int q = 0; q < kQ; ++q)
 #pragma unroll
       for (int b = 0; b < 4; ++b) ch += used((fw[q] >> (8 * b)) & 0xffu);
-    }
     int tot;
     int pos = tail_start + block_excl_scan(ch, misc + kMiscScanTail, lane, wave, &tot);  // (5)
 #pragma unroll
@@ -1210,19 +1226,11 @@ __global__ __launch_bounds__(kThreads) void resolve_direct_kernel(ResolveArgs a)
         pos += u ? 1 : 0;
       }
   }
-  // the stamps and the slot table written back as whole rows, 16 bytes per lane: the stamps of the used
-  // slots become t, the victims' entries their new tokens
+  // the slot table written back as whole rows, 16 bytes per lane: the victims' entries hold their new tokens
   if (kMode != kTrial) {
 #pragma unroll
     for (int q = 0; q < kQ; ++q) {
-      const uint32_t f = fw[q];
-      v4u ns;
-      ns.x = used(f & 0xffu) ? (uint32_t)t : sq[q].x;
-      ns.y = used((f >> 8) & 0xffu) ? (uint32_t)t : sq[q].y;
-      ns.z = used((f >> 16) & 0xffu) ? (uint32_t)t : sq[q].z;
-      ns.w = used(f >> 24) ? (uint32_t)t : sq[q].w;
       const uint32_t off = inq[q] ? 4u * (uint32_t)(s0 + 4 * q) : kNoAccess;
-      st128(ns, stamp_b, off);
       st128(*reinterpret_cast<const v4u*>(stok + (inq[q] ? s0 + 4 * q : 0)), stok_b, off);
     }
   }
