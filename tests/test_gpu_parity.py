@@ -238,6 +238,35 @@ def test_context_of_one_million_tokens(tail):
     p.close()
 
 
+def test_direct_layout_eight_slots_per_thread():
+    """B = 8192 with a short context: the direct layout with 8 ids and 8 slots per thread, every thread holding
+    two 4-slot chunks; fused resolve with a gather, then plan + copy, step by step against the oracle."""
+    import hierarchical_memory_amd as hm
+    H = 12000
+    w = workload.SINGLE_4K.with_(name="B8192", num_requests=2, top_k=2048, buffer_slots=8192, host_rows=H, L0=H,
+                                 window=6000, row_elems=32, steps=10, fused_gather=True)
+    sizes = hm.hs_required_sizes(hm.config(2, 2048, 8192, 0.0, 64, H))
+    assert sizes.token_slot_table == 3
+    ids = workload.streams(w)
+    ids[:, 1::3, 7] = ids[:, 1::3, 3]  # a repeated id now and then
+    p = Pair(w, ids=ids, gather=True)
+    p.run(check_every=1)
+    p.close()
+    p = Pair(w, ids=ids)
+    plan = p.sw.plan_buffer()
+    out, miss, status, _ = p.outs
+    for t in range(w.steps):
+        step_ids = p.ids[:, t]
+        hm.hs_plan(p.sw.ctx, torch.from_numpy(np.ascontiguousarray(step_ids)).cuda(), None, out, miss, status, plan)
+        hm.hs_copy(p.sw.ctx, plan, miss)
+        o_out, o_miss, o_status, _ = p.o.step(step_ids[p.sample])
+        assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+        assert (status.cpu().numpy() == o_status).all()
+        p.t += 1
+        p.check_state()
+    p.close()
+
+
 def test_single_request_full():
     p = Pair(workload.SINGLE_4K, gather=True)
     p.run(check_every=1)
