@@ -7,19 +7,21 @@
 // Mixed Residency. Two kernels do it, by LDS layout.
 //
 // resolve_direct_kernel (where a uint16 token -> slot entry for every host row fits in LDS):
-//   A  coalesced loads of the selected ids, the slot table and the LRU order list, all issued before any is
-//      consumed; each slot writes its index under its token in the (never cleared) token -> slot table;
+//   A  coalesced loads of the selected ids, the slot table, the LRU order list and the stamps, all issued before
+//      any is consumed; each slot writes its index under its token in the (never cleared) token -> slot table;
 //   B  each selected id is tested from its own side: it hits slot s = t2s[x] exactly when s < B and slot s
 //      holds x, so stale table entries cannot fake a hit; a hit marks its slot, a miss its bit in a bitmap
 //      of missed ids (an already-set bit or flag means the selection repeats an id, which is then ranked as
 //      in the rank kernel: the lowest position keeps it);
 //   C  one block scan ranks the misses (ascending id, popcounts of the bitmap) and the non-hit slots in LRU
 //      order; the first m of these are the victims, the others open the new order;
-//   D  j-th missed id -> j-th victim: page table, slot table, stamps, outputs; a second scan closes the new
-//      order with the slots used this step, in slot order;
+//   D  the used slots' stamp rows go out (whole rows, 16 bytes per lane); the j-th missed id takes the j-th
+//      victim: outputs, page table (fused), the LDS slot table; a second scan closes the new order with the
+//      slots used this step, in slot order; the slot-table rows go out;
 //   E  the missed rows are copied from mapped pinned host memory (and every selected row gathered when fused).
-// Ids and order entries stay in registers from A to D; the new order is staged in LDS and written at the end in
-// one 8-byte store per thread; there are six barriers.
+// Ids, order entries and stamps stay in registers from A to D. The new order is staged in LDS and written at
+// the end in one 8-byte store per thread, and a plan's victim lists go out densely after C: the kernel's phases
+// wait mostly on their vector-memory instructions, so each phase issues as few as it can. Six barriers.
 //
 // resolve_kernel (every shape, the rank layout):
 //   phase 0  the same loads, staged in LDS; ids classified and put into a bitmap of selected ids;
