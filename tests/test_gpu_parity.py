@@ -267,6 +267,59 @@ def test_direct_layout_eight_slots_per_thread():
     p.close()
 
 
+@pytest.mark.parametrize("H", [8192, 120_000], ids=["direct", "rank"])
+@pytest.mark.parametrize("path", ["fused", "plan_copy", "plan_copy_gather", "trial_commit", "static"])
+def test_degenerate_steps_every_path(path, H):
+    """Degenerate steps through every path of a step, against the oracle: a step of padding only, a step that
+    hits every id (no miss: empty plan lists, nothing to copy), a step of ids past the context (every one bad),
+    between ordinary steps; k 512, B 1024, with the token -> slot table (8192 rows) and without (120,000)."""
+    import hierarchical_memory_amd as hm
+    R, k, B = 3, 512, 1024
+    w = workload.SINGLE_4K.with_(name=f"degenerate_{path}_{H}", num_requests=R, top_k=k, buffer_slots=B,
+                                 host_rows=H, L0=H, window=2000, row_elems=32, steps=8, fused_gather=True)
+    sizes = hm.hs_required_sizes(hm.config(R, k, B, 0.0, 64, H))
+    assert sizes.token_slot_table == (3 if H == 8192 else 0)
+    ids = workload.streams(w)
+    ids[:, 2] = -1                      # padding only
+    ids[:, 3] = ids[:, 1]               # every id resident: no miss
+    ids[:, 4] = H + np.arange(k)        # every id past the context
+    ids[0, 5, :] = -1                   # one request padded, the others ordinary
+    gather = path in ("fused", "plan_copy_gather", "trial_commit", "static")
+    p = Pair(w, ids=ids, gather=gather)
+    out, miss, status, g = p.outs
+    plan = p.sw.plan_buffer() if path.startswith("plan") else None
+    trial = p.sw.trial_buffer() if path == "trial_commit" else None
+    for t in range(w.steps):
+        step_ids = np.ascontiguousarray(p.ids[:, t])
+        topk = torch.from_numpy(step_ids).cuda()
+        log(f"[degenerate {path} H={H}] step {t}")
+        if path == "fused":
+            hm.hs_resolve(p.sw.ctx, topk, None, out, miss, status, g)
+        elif path == "plan_copy":
+            hm.hs_plan(p.sw.ctx, topk, None, out, miss, status, plan)
+            hm.hs_copy(p.sw.ctx, plan, miss)
+        elif path == "plan_copy_gather":
+            hm.hs_plan(p.sw.ctx, topk, None, out, miss, status, plan, row_sources=True)
+            hm.hs_copy(p.sw.ctx, plan, miss, g)
+        elif path == "trial_commit":
+            hm.hs_trial(p.sw.ctx, topk, None, out, miss, status, g, trial)
+            hm.hs_commit(p.sw.ctx, trial, g)
+        else:
+            hm.hs_step_static(p.sw.ctx, topk, None, out, miss, status, g)
+        o_out, o_miss, o_status, o_g = p.o.step(step_ids[p.sample], gather=gather)
+        assert (out.cpu().numpy() == o_out).all(), f"step {t}: slots"
+        assert (miss.cpu().numpy() == o_miss).all() and (status.cpu().numpy() == o_status).all(), f"step {t}"
+        if gather:
+            assert (g.cpu().numpy() == o_g).all(), f"step {t}: gathered rows"
+        if t in (2, 3, 4):
+            assert (o_miss == 0).all()
+        if t == 4:
+            assert (o_status == hm.HS_STATUS_BAD_ID).all()
+        p.t += 1
+        p.check_state()
+    p.close()
+
+
 def test_single_request_full():
     p = Pair(workload.SINGLE_4K, gather=True)
     p.run(check_every=1)
