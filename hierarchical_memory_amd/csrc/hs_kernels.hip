@@ -352,6 +352,13 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
                     ((reinterpret_cast<uintptr_t>(a.order + rB) & 7) == 0);
   const bool veck = (k & 3) == 0 && ((reinterpret_cast<uintptr_t>(a.topk + rk) & 15) == 0);
   const int n4B = vecB ? (B >> 2) : 0, n4k = veck ? (k >> 2) : 0;
+  // B = 4 x threads with aligned rows: thread tid owns slots 4 tid .. 4 tid + 3, and writes their stamps and
+  // slot-table entries back as whole 16-byte rows (the old stamps loaded with the first round of loads): one
+  // store instruction per wave for each table instead of one masked instruction per slot. (Staging the new
+  // order in LDS for 8-byte stores, as the direct layout does, measured slower here: its extra barrier costs
+  // more than the stores it saves.)
+  const bool stamp_rows = kMode != kTrial && B == 4 * kThreads && vecB &&
+                          (reinterpret_cast<uintptr_t>(stamp_r) & 15) == 0;
   const int4* st4 = reinterpret_cast<const int4*>(a.slot_tok + rB);
   const uint2* or4 = reinterpret_cast<const uint2*>(a.order + rB);
   const int4* tk4 = reinterpret_cast<const int4*>(a.topk + rk);
@@ -359,6 +366,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   uint2 o0 = make_uint2(0u, 0u);
   if (tid < n4B) { y0 = st4[tid]; o0 = or4[tid]; }
   if (tid < n4k) x0 = tk4[tid];
+  v4u sp0 = {0u, 0u, 0u, 0u};  // the old stamps of the thread's four slots, for the stamp rows
+  if (stamp_rows) sp0 = reinterpret_cast<const v4u*>(stamp_r)[tid];
   {
     // the two bitmaps are adjacent, each padded to 16 bytes: cleared together in 16-byte stores
     uint4* bm = reinterpret_cast<uint4*>(smem + L.sel);
@@ -601,6 +610,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   }
   if (st) atomicOr(&misc[kMiscStatus], st);
 
+  auto used = [&](uint32_t f) { return fifo ? f == 2u : f != 0u; };
+
   // ---- phase 3: ranks of the misses (ascending id) and of the non-hit slots in LRU order, in one scan
   // (misses in the low 16 bits: m <= k <= 8192; candidates in the high 16 bits: <= B <= 65535)
   int m, ncand;
@@ -694,6 +705,18 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   }
   __syncthreads();
   const uint32_t t0m = ring_base(has_tail, t0, T);  // x mod T = (t0m + x - t0) mod T for a resident x
+  // the slot flags are final: the stamp rows go out now, ahead of the pairing (every row, used slots or not:
+  // measured faster than predicating the store on the row holding a used slot)
+  uint32_t f4 = 0u;  // a whole chunk's four flags, one byte each
+  if (whole4) f4 = *reinterpret_cast<const uint32_t*>(sflag + s0);
+  if (stamp_rows) {
+    v4u ns = sp0;
+    if (used(f4 & 0xffu)) ns.x = (uint32_t)t;
+    if (used((f4 >> 8) & 0xffu)) ns.y = (uint32_t)t;
+    if (used((f4 >> 16) & 0xffu)) ns.z = (uint32_t)t;
+    if (used(f4 >> 24)) ns.w = (uint32_t)t;
+    __builtin_nontemporal_store(ns, reinterpret_cast<v4u*>(stamp_r) + tid);
+  }
 
   // ---- phase 4: pair misses with victims: outputs and page table; the victims' new tokens go to the LDS
   // copy of the slot table, written back below as coalesced rows
@@ -741,11 +764,8 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
   // (FIFO); the scan's barrier also publishes the LDS writes above
   const int tail_start = fifo ? B - m : ncand - m;
   {
-    auto used = [&](uint32_t f) { return fifo ? f == 2u : f != 0u; };
     int ch = 0;
-    uint32_t f4 = 0u;  // a whole chunk's four flags, one byte each
     if (whole4) {
-      f4 = *reinterpret_cast<const uint32_t*>(sflag + s0);
 #pragma unroll
       for (int u = 0; u < 4; ++u) ch += used((f4 >> (8 * u)) & 0xffu);
     } else {
@@ -766,9 +786,12 @@ __global__ __launch_bounds__(kThreads) void resolve_kernel(ResolveArgs a) {
         if (used(sflag[s])) append(s);
     }
   }
-  // stamps of hit and victim slots, and the victims' slot-table entries: consecutive lanes write
-  // consecutive slots
-  if (kMode != kTrial) {
+  // stamps of hit and victim slots, and the victims' slot-table entries: whole rows that hold a victim, or
+  // with consecutive lanes on consecutive slots
+  if (stamp_rows) {
+    if ((f4 & 0x02020202u) != 0u)
+      __builtin_nontemporal_store(*reinterpret_cast<const v4u*>(stok + s0), reinterpret_cast<v4u*>(slot_tok_r) + tid);
+  } else if (kMode != kTrial) {
     for (int s = tid; s < B; s += kThreads) {
       const uint8_t f = sflag[s];
       if (fifo ? f == 2 : f != 0) at(stamp_r, s) = t;
