@@ -320,6 +320,58 @@ def test_degenerate_steps_every_path(path, H):
     p.close()
 
 
+@pytest.mark.parametrize("policy", [0, 1], ids=["lru", "fifo"])
+@pytest.mark.parametrize("path", ["fused", "fused_gather", "plan_copy", "trial_commit", "static"])
+def test_rank_layout_four_slots_per_thread(path, policy):
+    """The rank layout at B = 4096 (four slots per thread: stamps and slot-table entries written back as whole
+    16-byte rows) through every path of a step, LRU and FIFO, against the oracle: k 2048, a 150,000-token
+    context (no room for a token -> slot table) with a 2048-token device tail; repeated ids, padding and bad
+    ids on some steps, and a step that hits every id."""
+    import hierarchical_memory_amd as hm
+    R, k, B, H, T = 2, 2048, 4096, 150_000, 2048
+    w = workload.SINGLE_4K.with_(name=f"rank_rows_{path}_{policy}", num_requests=R, top_k=k, buffer_slots=B,
+                                 host_rows=H, L0=H, window=6000, partB_permille=200, row_elems=32, steps=8,
+                                 fused_gather=True, tail_tokens=T)
+    sizes = hm.hs_required_sizes(hm.config(R, k, B, 0.0, 64, H, T, policy))
+    assert sizes.token_slot_table == 0 and sizes.sparse_rank == 0
+    ids = workload.streams(w)
+    ids[:, 2, 7] = ids[:, 2, 3]          # a repeated id
+    ids[:, 3, :100] = -1                 # padding
+    ids[:, 3, 100:105] = H + 5           # bad ids
+    ids[:, 5] = ids[:, 4]                # every id hit
+    gather = path != "fused" and path != "plan_copy"
+    p = Pair(w, ids=ids, gather=gather, policy=policy)
+    out, miss, status, g = p.outs
+    plan = p.sw.plan_buffer() if path == "plan_copy" else None
+    trial = p.sw.trial_buffer() if path == "trial_commit" else None
+    for t in range(w.steps):
+        step_ids = np.ascontiguousarray(p.ids[:, t])
+        topk = torch.from_numpy(step_ids).cuda()
+        log(f"[rank rows {path} policy={policy}] step {t}")
+        if path == "fused":
+            hm.hs_resolve(p.sw.ctx, topk, p.tail0_dev, out, miss, status)
+        elif path == "fused_gather":
+            hm.hs_resolve(p.sw.ctx, topk, p.tail0_dev, out, miss, status, g)
+        elif path == "plan_copy":
+            hm.hs_plan(p.sw.ctx, topk, p.tail0_dev, out, miss, status, plan)
+            hm.hs_copy(p.sw.ctx, plan, miss)
+        elif path == "trial_commit":
+            hm.hs_trial(p.sw.ctx, topk, p.tail0_dev, out, miss, status, g, trial)
+            hm.hs_commit(p.sw.ctx, trial, g)
+        else:
+            hm.hs_step_static(p.sw.ctx, topk, p.tail0_dev, out, miss, status, g)
+        o_out, o_miss, o_status, o_g = p.o.step(step_ids[p.sample], p.tail0[p.sample], gather=gather)
+        assert (out.cpu().numpy() == o_out).all(), f"step {t}: slots"
+        assert (miss.cpu().numpy() == o_miss).all() and (status.cpu().numpy() == o_status).all(), f"step {t}"
+        if gather:
+            assert (g.cpu().numpy() == o_g).all(), f"step {t}: gathered rows"
+        if t == 5:
+            assert (o_miss == 0).all()
+        p.t += 1
+        p.check_state()
+    p.close()
+
+
 def test_single_request_full():
     p = Pair(workload.SINGLE_4K, gather=True)
     p.run(check_every=1)
