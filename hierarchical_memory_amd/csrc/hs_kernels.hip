@@ -57,6 +57,7 @@ enum : int8_t { C_PAD = 0, C_BAD = 1, C_DUP = 2, C_RES = 3, C_CAND = 4 };
 
 constexpr int kStatusBadId = 1, kStatusDupId = 2, kStatusBadState = 4, kStatusStale = 8;
 constexpr int kUnroll = 4;  // 16-byte loads each thread keeps in flight in the gather loop
+constexpr int kCommitUnroll = 2;  // the same in the commit's row copy (measured: 2 beats 4 and 8)
 
 // misc words in LDS: one slot array of wave totals per block scan, per-wave flag words, then single words
 constexpr int kMiscScanSel = 0, kMiscScanRank = kWaves, kMiscScanTail = 2 * kWaves, kMiscWaveBad = 3 * kWaves,
@@ -1480,34 +1481,48 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
   // the misses' victim slots and gather positions, staged for the row copy (after the B flags, 4-aligned)
   int32_t* lslot = reinterpret_cast<int32_t*>(smem + ((a.B + 3) & ~3));
   int32_t* lpos = lslot + a.k;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  if (a.accept && a.accept[r] == 0) {
-    if (a.status && tid == 0) a.status[r] = 0;
-    return;
-  }
+  const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int k = a.k, B = a.B, H = a.H;
   const int32_t* rec = a.trial + (size_t)r * a.trial_words;
-  const int m = rec[0], u0 = rec[1], t = rec[2];
-  if (t < 0 || a.step[r] != t || a.epoch[r] != rec[3] || m < 0 || m > k || u0 < 0 || u0 > B) {
-    if (a.status && tid == 0) a.status[r] = kStatusStale;
-    return;
-  }
-  const size_t rB = (size_t)r * B, rH = (size_t)r * H, rk = (size_t)r * k;
   const uint16_t* nord = reinterpret_cast<const uint16_t*>(rec + kTrialHead + 4 * k);
   const int32_t* tok = rec + kTrialHead;
   const int32_t* slot = tok + k;
   const int32_t* evicted = slot + k;
   const int32_t* pos = evicted + k;
-  const int nt = blockDim.x;
-  // The first round of every record load (four order entries and one miss per thread) is issued before the
-  // flags are cleared, so the two lists cost one round trip; later rounds, for larger shapes, load as they go.
+  const size_t rB = (size_t)r * B, rH = (size_t)r * H, rk = (size_t)r * k;
+  // One round of independent loads: the accept flag, the record's header, the request's step and change
+  // counter, four order entries and one miss entry per thread (a miss entry is read before m is known, from
+  // the record's k entries, and used only below m). The flags are cleared while they are in flight.
+  const int acc = a.accept ? a.accept[r] : 1;
+  const int m = rec[0], u0 = rec[1], t = rec[2], rec_epoch = rec[3];
+  const int cur_step = a.step[r], cur_epoch = a.epoch[r];
   int o0[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) o0[u] = tid + u * nt < B ? nord[tid + u * nt] : B;
   int x0 = -1, v0 = -1, y0 = -1, i0 = -1;
-  if (tid < m) { x0 = tok[tid]; v0 = slot[tid]; y0 = evicted[tid]; i0 = pos[tid]; }
+  if (tid < k) { x0 = tok[tid]; v0 = slot[tid]; y0 = evicted[tid]; i0 = pos[tid]; }
   for (int s = tid; s < B; s += nt) used[s] = 0;
-  __syncthreads();
+  if (acc == 0) {
+    if (a.status && tid == 0) a.status[r] = 0;
+    return;
+  }
+  if (t < 0 || cur_step != t || cur_epoch != rec_epoch || m < 0 || m > k || u0 < 0 || u0 > B) {
+    if (a.status && tid == 0) a.status[r] = kStatusStale;
+    return;
+  }
+  // the victims' table entries, and their slots and gather positions staged for the row copy
+  auto miss_entry = [&](int j, int x, int v, int y, int i) {
+    const bool ok = x >= 0 && x < H && v >= 0 && v < B;
+    lslot[j] = ok && i >= 0 && i < k ? v : -1;  // a row only for a sound entry
+    lpos[j] = i;
+    if (!ok) return;
+    if (y >= 0 && y < H) a.page[rH + y] = -1;
+    a.page[rH + x] = v;
+    a.slot_tok[rB + v] = x;
+  };
+  if (tid < m) miss_entry(tid, x0, v0, y0, i0);
+  for (int j = tid + nt; j < m; j += nt) miss_entry(j, tok[j], slot[j], evicted[j], pos[j]);
+  __syncthreads();  // the staged slots and positions, and the cleared flags
   // the new order and its tail's flags
   auto place = [&](int p, int o) {
     if (p >= B || o >= B) return;  // past the end, or a corrupt record
@@ -1525,29 +1540,14 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) place(p0 + u * nt, o[u]);
   }
-  // the victims' table entries, and their slots and gather positions staged for the row copy
-  auto miss_entry = [&](int j, int x, int v, int y, int i) {
-    const bool ok = x >= 0 && x < H && v >= 0 && v < B;
-    lslot[j] = ok && i >= 0 && i < k ? v : -1;  // a row only for a sound entry
-    lpos[j] = i;
-    if (!ok) return;
-    if (y >= 0 && y < H) a.page[rH + y] = -1;
-    a.page[rH + x] = v;
-    a.slot_tok[rB + v] = x;
-  };
-  if (tid < m) miss_entry(tid, x0, v0, y0, i0);
-  for (int j = tid + nt; j < m; j += nt) miss_entry(j, tok[j], slot[j], evicted[j], pos[j]);
-  __syncthreads();
-  for (int s = tid; s < B; s += nt)
-    if (used[s]) a.stamp[rB + s] = t;
-  // missed rows, gather output -> victim slots: the slot and position of a chunk come from LDS, so each
-  // thread keeps kUnroll 16-byte loads in flight with nothing between them
+  // missed rows, gather output -> victim slots, while the table stores drain: the slot and position of a
+  // chunk come from LDS, kCommitUnroll 16-byte loads in flight per thread
   const int row16 = a.row16, total = m * row16;
-  for (int c0 = tid; c0 < total; c0 += nt * kUnroll) {
-    v4u val[kUnroll];
-    int64_t dst[kUnroll];
+  for (int c0 = tid; c0 < total; c0 += nt * kCommitUnroll) {
+    v4u val[kCommitUnroll];
+    int64_t dst[kCommitUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kCommitUnroll; ++u) {
       const int c = c0 + u * nt;
       dst[u] = -1;
       if (c < total) {
@@ -1560,9 +1560,12 @@ __global__ __launch_bounds__(1024) void commit_kernel(CommitArgs a) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < kCommitUnroll; ++u)
       if (dst[u] >= 0) a.hot[dst[u]] = val[u];
   }
+  __syncthreads();  // the tail's flags
+  for (int s = tid; s < B; s += nt)
+    if (used[s]) a.stamp[rB + s] = t;
   if (tid == 0) {
     a.step[r] = t + 1;
     if (a.status) a.status[r] = 0;
