@@ -29,11 +29,17 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E (published)
 
 
 def kernel_source_digest() -> str:
+    """Digest of the kernel sources' code: comments and blank lines are left out, so a comment edit keeps a
+    traffic record taken on the same code valid, and any change to the code itself does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("hs_kernels.hip", "hs_internal.h"):
-        with open(os.path.join(ROOT, "hierarchical_memory_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "hierarchical_memory_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments (no string literal holds one)
+        lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+        h.update("\n".join(ln for ln in lines if ln.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -31,7 +31,8 @@
 //            the bitmap: a hit, recorded under the token's rank and marked in a hit bitmap;
 //   phase 3  one block scan ranks the misses (selected ids outside the tail window and not hit) and the
 //            non-hit slots in LRU order, as in C above;
-//   phase 4  as D above;
+//   phase 4  as D above (where B is four slots per thread, the stamps and slot-table entries go back as whole
+//            16-byte rows, the stamp rows right after phase 3; elsewhere one store per used slot);
 //   phase 5  as E above.
 // Scans run over thread-contiguous chunks: a DPP scan inside each wave, one exchange of the 16 wave totals
 // through LDS, which each wave scans again in one DPP row. No result depends on the order of LDS atomics
