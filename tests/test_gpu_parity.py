@@ -72,7 +72,7 @@ def _random_shape(seed):
     return rng, R, k, B, H, T, rb, policy, gather
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_shapes(seed):
     """Seeded random shapes (k, B, context, tail, row size, policy, fused gather), with padding, bad and repeated
     ids, k and B off the 16-byte vector path; every step and the final state against the oracle."""
@@ -88,7 +88,7 @@ def test_random_shapes(seed):
     p.close()
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(32))
 def test_random_shapes_rank_layout(seed):
     """Small random k and B with a long context (H >= 82,000: no room for a token -> slot table), so every
     launch takes the rank layout; ids drawn from a window of about 3B tokens so that slots are hit, with
@@ -150,7 +150,7 @@ def test_context_of_262144_tokens():
     p.close()
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_shapes_sparse_layout(seed):
     """Contexts of 600,000 to 1,200,000 tokens with small k and B: past the flat bitmaps' LDS, so every launch
     takes the two-level rank layout. Most ids come from a window of about 3B tokens (slots are hit), the rest

@@ -66,7 +66,7 @@ def _eq(got, exp, what, op, n):
     assert (got == exp).all(), f"call {n} ({op}): {what} differs at {np.argwhere(got != exp)[:5].tolist()}"
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_call_sequences(seed):
     import hierarchical_memory_amd as hm
     rng = np.random.default_rng(500 + seed)
