@@ -705,12 +705,25 @@ def trial_leg(hm, torch, np, sw, topk, tail0, W, K, w):
     commit_ms = np.array([eb[i].elapsed_time(ea[i + 1]) for i in range(K)])
     total = ea[0].elapsed_time(ea[K])
     mean_m = miss[W:].cpu().numpy().astype(np.int64).sum() / K
+    # the commit's bytes per launch: each missed row read from the gather output and written to its slot, the
+    # record's four lists and the table entries of each miss (page table twice, slot table), the order list
+    # read from the record and written, the record header, and the stamps of the slots used this step (hits
+    # and misses, counted on the last step's outputs)
+    used = int(((out >= 0) & (out < w.buffer_slots)).sum().item())
+    commit_bytes = mean_m * (2 * rb + 16 + 12) + R * (4 * w.buffer_slots + 16) + 4 * used
+    commit_avg = float(commit_ms.mean())
+    commit_gbps = commit_bytes / (commit_avg / 1e3) / 1e9
     del g
     log(f"[bench] trial+commit: {total / K:.3f} ms/step (trial {trial_ms.mean() * 1e3:.0f} us, commit "
-        f"{commit_ms.mean() * 1e3:.0f} us)")
+        f"{commit_avg * 1e3:.0f} us, {commit_gbps:.0f} GB/s)")
     return {"steps": K, "warmup": W, "step_ms": total / K, "trial_avg_us": float(trial_ms.mean()) * 1e3,
-            "commit_avg_us": float(commit_ms.mean()) * 1e3,
-            "entries_per_s": K * R * k / (total / 1e3), "miss_rows_per_request_step": mean_m / R}
+            "commit_avg_us": commit_avg * 1e3,
+            "entries_per_s": K * R * k / (total / 1e3), "miss_rows_per_request_step": mean_m / R,
+            "commit": {"kernel": "commit_kernel (hs_commit)", "bound": "hbm", "achieved": commit_gbps,
+                       "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": commit_gbps / HBM_PEAK_GBPS,
+                       "algorithmic_bytes_per_launch": commit_bytes,
+                       "bytes_model": "per request 2 row + 28 bytes per miss, 4B + 16 of order list and header, "
+                                      "4 per used slot (the last step's count)"}}
 
 
 def main() -> int:
