@@ -281,6 +281,7 @@ struct ResetArgs {
 constexpr int kCopyUnroll = 8;
 constexpr int kCopyWorkgroups = 128;
 constexpr int kCopyThreads = 64;
+constexpr int kBatchRows = 512;  // the balanced copy (fewer requests than workgroups): rows located per batch
 
 // gather_kernel: threads per workgroup, 16-byte loads in flight per thread, and the chunks one workgroup
 // covers (its row count is the largest that fits, at least one)

@@ -481,8 +481,49 @@ def test_maximum_request_count():
     assert (st.cpu().numpy() == p.o.offload(rows, pos)).all()
     torch.cuda.synchronize()
     assert (p.sw.host_pool() == p.o.host).all()
-    for _ in range(2, steps):
+    # a step through plan + copy without a gather (workgroups bound to requests)
+    topk = torch.from_numpy(np.ascontiguousarray(p.ids[:, 2])).cuda()
+    hm.hs_plan(p.sw.ctx, topk, None, out, miss, status, plan)
+    hm.hs_copy(p.sw.ctx, plan, miss)
+    o_out, o_miss, _, _ = p.o.step(p.ids[:, 2])
+    assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+    p.t += 1
+    p.check_state()
+    for _ in range(3, steps):
         p.step(check_state=True)
+    p.close()
+
+
+@pytest.mark.parametrize("R", [1, 2, 33, 127, 128, 129, 300])
+def test_plan_then_copy_request_counts(R):
+    """hs_plan + hs_copy without a gather on either side of the copy's two grids (with fewer requests than its
+    128 workgroups every workgroup takes an equal share of the step's missed rows; with more, workgroups are
+    bound to requests): one request padded and one hitting every id at one step, so some requests have no
+    miss; every request's outputs, tables and rows against the oracle."""
+    import hierarchical_memory_amd as hm
+    rng = np.random.default_rng(4000 + R)
+    k, B, H, rb, steps = 24, 48, 160, 48, 4
+    w = workload.SINGLE_4K.with_(name=f"copy_R{R}", num_requests=R, top_k=k, buffer_slots=B, host_rows=H, L0=H,
+                                 row_elems=rb // 2, steps=steps, fused_gather=False)
+    ids = np.stack([np.stack([rng.choice(H, size=k, replace=False) for _ in range(steps)]) for _ in range(R)])
+    ids = ids.astype(np.int32)
+    ids[0, 2] = -1                      # request 0: padding only at step 2
+    if R > 1:
+        ids[R - 1, 2] = ids[R - 1, 1]   # the last request: every id hit at step 2
+    p = Pair(w, ids=ids, gather=False)  # every request against the oracle
+    out, miss, status, _ = p.outs
+    plan = p.sw.plan_buffer()
+    for t in range(steps):
+        step_ids = np.ascontiguousarray(p.ids[:, t])
+        hm.hs_plan(p.sw.ctx, torch.from_numpy(step_ids).cuda(), None, out, miss, status, plan)
+        hm.hs_copy(p.sw.ctx, plan, miss)
+        o_out, o_miss, o_status, _ = p.o.step(step_ids)
+        assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+        assert (status.cpu().numpy() == o_status).all()
+        if t == 2:
+            assert o_miss[0] == 0 and o_miss[R - 1] == 0
+        p.t += 1
+        p.check_state()
     p.close()
 
 
