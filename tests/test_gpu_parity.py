@@ -577,18 +577,40 @@ def test_padding_bad_and_repeated_ids():
     p.close()
 
 
-def test_corrupt_state_is_reported_not_used():
+@pytest.mark.parametrize("path", ["fused", "plan_copy", "trial_commit"])
+def test_corrupt_state_is_reported_not_used(path):
+    """A request whose slot table holds an impossible token is refused by every path of a step (status
+    HS_STATUS_BAD_STATE, no miss, outputs -1, its state untouched: no row copied, no record committed) while
+    the other requests step as the oracle does."""
     import hierarchical_memory_amd as hm
     w = workload.SINGLE_4K.with_(num_requests=3, steps=4)
-    p = Pair(w, sample=[0, 2])
+    p = Pair(w, sample=[0, 2], gather=path == "trial_commit")
     p.step()
     # corrupt request 1's slot table from the host: the kernel must refuse it and leave its state alone
     p.sw.slot_tok[1, 5] = w.host_rows + 7
-    before = [t.clone() for t in (p.sw.slot_tok, p.sw.stamp, p.sw.page, p.sw.step, p.sw.hot)]
-    p.step()
-    out, miss, status, _ = p.outs
+    before = [t.clone() for t in (p.sw.slot_tok, p.sw.stamp, p.sw.page, p.sw.step, p.sw.hot, p.sw.lru_order)]
+    out, miss, status, g = p.outs
+    if path == "fused":
+        p.step()
+    else:
+        step_ids = np.ascontiguousarray(p.ids[:, p.t])
+        topk = torch.from_numpy(step_ids).cuda()
+        if path == "plan_copy":
+            plan = p.sw.plan_buffer()
+            hm.hs_plan(p.sw.ctx, topk, None, out, miss, status, plan)
+            hm.hs_copy(p.sw.ctx, plan, miss)
+        else:
+            trial = p.sw.trial_buffer()
+            cstat = torch.zeros(3, dtype=torch.int32, device="cuda")
+            hm.hs_trial(p.sw.ctx, topk, None, out, miss, status, g, trial)
+            hm.hs_commit(p.sw.ctx, trial, g, None, cstat)
+            assert cstat[1].item() == hm.HS_STATUS_STALE and cstat[0].item() == 0 and cstat[2].item() == 0
+        o_out, o_miss, o_status, _ = p.o.step(step_ids[p.sample])
+        assert (out.cpu().numpy()[p.sample] == o_out).all() and (miss.cpu().numpy()[p.sample] == o_miss).all()
+        assert (status.cpu().numpy()[p.sample] == o_status).all()
+        p.t += 1
     assert status[1].item() == hm.HS_STATUS_BAD_STATE and miss[1].item() == 0 and (out[1] == -1).all()
-    for b, a in zip(before, (p.sw.slot_tok, p.sw.stamp, p.sw.page, p.sw.step, p.sw.hot)):
+    for b, a in zip(before, (p.sw.slot_tok, p.sw.stamp, p.sw.page, p.sw.step, p.sw.hot, p.sw.lru_order)):
         assert torch.equal(b[1], a[1])
     p.check_state()
     p.close()
