@@ -1235,6 +1235,40 @@ def test_large_topk_equal_buffer():
     p.close()
 
 
+@pytest.mark.parametrize("path", ["fused", "fused_gather", "plan_copy"])
+def test_largest_topk_and_buffer(path):
+    """k = 4096 with B = 8192 and a 40,000-token context, near the LDS cap of one workgroup (the direct layout
+    with eight ids and eight slots per thread without a gather, the rank layout with one), a repeated id on
+    some steps; every step and the state against the oracle."""
+    import hierarchical_memory_amd as hm
+    R, k, B, H = 2, 4096, 8192, 40_000
+    sizes = hm.hs_required_sizes(hm.config(R, k, B, 0.0, 64, H))
+    assert sizes.lds_bytes > 150 * 1024 and sizes.token_slot_table == 1
+    w = workload.SINGLE_4K.with_(name=f"k4096_B8192_{path}", num_requests=R, top_k=k, buffer_slots=B,
+                                 host_rows=H, L0=H, window=12000, row_elems=32, steps=8,
+                                 fused_gather=path == "fused_gather")
+    ids = workload.streams(w)
+    ids[:, 1::3, 11] = ids[:, 1::3, 2]
+    if path != "plan_copy":
+        p = Pair(w, ids=ids, gather=path == "fused_gather")
+        p.run(check_every=1)
+        p.close()
+        return
+    p = Pair(w, ids=ids)
+    plan = p.sw.plan_buffer()
+    out, miss, status, _ = p.outs
+    for t in range(w.steps):
+        step_ids = np.ascontiguousarray(p.ids[:, t])
+        hm.hs_plan(p.sw.ctx, torch.from_numpy(step_ids).cuda(), None, out, miss, status, plan)
+        hm.hs_copy(p.sw.ctx, plan, miss)
+        o_out, o_miss, o_status, _ = p.o.step(step_ids[p.sample])
+        assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+        assert (status.cpu().numpy() == o_status).all()
+        p.t += 1
+        p.check_state()
+    p.close()
+
+
 def test_many_small_requests():
     """1500 requests (1500 workgroups, more than the 256 CUs), tiny k and B."""
     rng = np.random.default_rng(8)
