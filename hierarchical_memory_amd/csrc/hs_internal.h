@@ -275,9 +275,10 @@ struct ResetArgs {
   int32_t* epoch;      // [R] change counters, advanced (nullptr: leave them)
 };
 
-// copy_kernel: 16-byte host loads each thread keeps in flight, threads per workgroup (one wave) and the number
-// of workgroups (measured: 128 one-wave workgroups hold the host link's rate within 2 % of the best grid, and
-// disturb HBM-bound work on other streams far less than fewer, larger workgroups with as many loads in flight)
+// copy_kernel and copy_balanced_kernel: 16-byte host loads each thread keeps in flight, threads per workgroup
+// (one wave) and the number of workgroups (measured: 128 one-wave workgroups hold the host link's rate within 2 %
+// of the best grid, and disturb HBM-bound work on other streams far less than fewer, larger workgroups with as
+// many loads in flight)
 constexpr int kCopyUnroll = 8;
 constexpr int kCopyWorkgroups = 128;
 constexpr int kCopyThreads = 64;
