@@ -214,13 +214,16 @@ int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32
  * host pool into its slot, the evicted tokens' page entries become -1 and the missed tokens' entries their
  * slots (the page table is not read on the decode path, so its scattered updates ride with the link-bound
  * copy instead of the plan). Without d_gather the copy runs on a bounded grid of 128 one-wave workgroups,
- * which holds the host link's rate and leaves the compute units to work on other streams. With d_gather
- * (nullable, [R][k][row_bytes], 16-byte aligned) it also writes every selected row there, as hs_resolve's fused gather does, in workgroups spread over the whole chip (the
- * missed rows straight from the host pool); that needs a plan made with HS_PLAN_ROW_SOURCES (other plans give
- * undefined rows, never an access out of bounds). Until hs_copy completes, the hot rows of this step's new
- * slots are stale and the page table does not show the step. Two plans may run back to back, but the copy of
- * a step must complete before the copy of the next step and before any call other than hs_plan reads or
- * writes the context's state.
+ * which holds the host link's rate and leaves the compute units to work on other streams (with fewer requests
+ * than workgroups, the step's missed rows are shared out evenly over them). With d_gather (nullable,
+ * [R][k][row_bytes], 16-byte aligned) it also writes every selected row there, as hs_resolve's fused gather
+ * does, in workgroups spread over the whole chip (the missed rows straight from the host pool); that needs a
+ * plan made with HS_PLAN_ROW_SOURCES (other plans give undefined rows, never an access out of bounds).
+ * hs_copy reads d_plan and d_miss as hs_plan left them: on another stream it must be ordered after the plan
+ * (an event recorded after hs_plan, waited on by the copy's stream). Until hs_copy completes, the hot rows of
+ * this step's new slots are stale and the page table does not show the step. Two plans may run back to back,
+ * but the copy of a step must complete before the copy of the next step and before any call other than
+ * hs_plan reads or writes the context's state.
  */
 #define HS_PLAN_ROW_SOURCES 1 /* hs_plan flag: also record each position's row source (for a gathering hs_copy) */
 int hs_plan(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32_t* d_out, int32_t* d_miss,
