@@ -285,9 +285,13 @@ constexpr int kCopyThreads = 64;
 constexpr int kBatchRows = 512;  // the balanced copy (fewer requests than workgroups): rows located per batch
 
 // gather_kernel: threads per workgroup, 16-byte loads in flight per thread, and the chunks one workgroup
-// covers (its row count is the largest that fits, at least one)
-constexpr int kGatherThreads = 256;
-constexpr int kGatherUnroll = 3;
+// covers (its row count is the largest that fits, at least one). Measured with 1152-byte rows, TB/s on the
+// 256-, 32- and 64-request (device tail) workloads: 128 x 2 (3 rows per workgroup) 6.11-6.16 / 5.55 /
+// 5.89-5.90; 256 x 3 6.02-6.05 / 5.43-5.44 / 5.77-5.79; 128 x 4 6.09-6.10 / 5.41-5.43 / 5.69; 256 x 2
+// 5.98-6.00 / 5.46 / 5.87; 512 x 1 6.07 / 5.42-5.43 / 5.18-5.20. The gathering copy (hs_copy with a gather
+// output) is the same at every shape.
+constexpr int kGatherThreads = 128;
+constexpr int kGatherUnroll = 2;
 constexpr int kGatherChunks = kGatherThreads * kGatherUnroll;
 
 struct GatherArgs {
