@@ -217,8 +217,10 @@ int hs_resolve(hs_ctx* ctx, const int32_t* d_topk, const int32_t* d_tail0, int32
  * which holds the host link's rate and leaves the compute units to work on other streams (with fewer requests
  * than workgroups, the step's missed rows are shared out evenly over them). With d_gather (nullable,
  * [R][k][row_bytes], 16-byte aligned) it also writes every selected row there, as hs_resolve's fused gather
- * does, in workgroups spread over the whole chip (the missed rows straight from the host pool); that needs a
- * plan made with HS_PLAN_ROW_SOURCES (other plans give undefined rows, never an access out of bounds).
+ * does, in workgroups spread over the whole chip (the missed rows straight from the host pool, and into their
+ * slots from the positions that gather them); that needs a plan made with HS_PLAN_ROW_SOURCES (with another
+ * plan the gathered rows and the new slots' rows are undefined, never an access out of bounds; the page table
+ * and every other table are still exact).
  * hs_copy reads d_plan and d_miss as hs_plan left them: on another stream it must be ordered after the plan
  * (an event recorded after hs_plan, waited on by the copy's stream). Until hs_copy completes, the hot rows of
  * this step's new slots are stale and the page table does not show the step. Two plans may run back to back,

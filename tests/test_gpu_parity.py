@@ -800,10 +800,44 @@ def test_plan_then_copy_matches_oracle():
 COPY_GATHER_CASES = [  # (k, B, H, T, row_bytes, policy)
     (200, 330, 1500, 0, 80, 0),
     (200, 330, 1500, 40, 80, 0),  # device tail
-    (33, 40, 300, 7, 1152, 1),  # 10 rows per workgroup, the last of 4 holds 3; FIFO
-    (5, 8, 60, 3, 16384, 0),  # 1024 chunks per row: one row per workgroup in two passes
+    (34, 40, 300, 7, 1152, 1),  # 3 rows per workgroup, the last of 12 holds 1; FIFO
+    (5, 8, 60, 3, 16384, 0),  # 1024 chunks per row: one row per workgroup in four passes
     (2, 4, 6, 1, 1 << 20, 1),  # the largest row (1 MiB); FIFO
 ]
+
+
+def test_gathering_copy_of_a_plan_without_row_sources():
+    """hs_copy with a gather output takes each position's row source from the plan, and writes a missed row to
+    its slot from the position that gathers it; a plan made without HS_PLAN_ROW_SOURCES leaves that part as it
+    was (here: arbitrary values, in and out of every range). The gathered rows and the new slots' rows are then
+    undefined, but every access stays in bounds, the page table is published from the miss list, and the
+    outputs and every table match the oracle."""
+    import hierarchical_memory_amd as hm
+    rng = np.random.default_rng(77)
+    R, k, B, H, T, rb = 3, 64, 128, 1000, 16, 48
+    w = workload.SINGLE_4K.with_(name="copy_without_sources", num_requests=R, top_k=k, buffer_slots=B,
+                                 host_rows=H, L0=H, tail_tokens=T, row_elems=rb // 2, window=400, steps=5,
+                                 partB_permille=200, fused_gather=True)
+    p = Pair(w, gather=True)
+    out, miss, status, g = p.outs
+    plan = p.sw.plan_buffer()
+    edges = np.array([-2 - k - 5, -2 - k, -3 - k, -2, -1, 0, B - 1, B, B + T - 1, B + T, B + T + 7, 1 << 30,
+                      -(1 << 30)], np.int32)
+    for t in range(w.steps):
+        src = rng.integers(-5000, 5000, size=(R, k)).astype(np.int32)
+        src[:, :len(edges)] = edges
+        plan[:, 3].copy_(torch.from_numpy(src))
+        step_ids = np.ascontiguousarray(p.ids[:, t])
+        hm.hs_plan(p.sw.ctx, torch.from_numpy(step_ids).cuda(), p.tail0_dev, out, miss, status, plan)
+        hm.hs_copy(p.sw.ctx, plan, miss, g)
+        o_out, o_miss, o_status, _ = p.o.step(step_ids, p.tail0)
+        assert (out.cpu().numpy() == o_out).all() and (miss.cpu().numpy() == o_miss).all()
+        assert (status.cpu().numpy() == o_status).all()
+        p.t += 1
+        for name, got, exp in (("slot_tok", p.sw.slot_tok, p.o.slot_tok), ("stamp", p.sw.stamp, p.o.stamp),
+                               ("page", p.sw.page, p.o.page), ("step", p.sw.step, p.o.t)):
+            assert (got.cpu().numpy() == exp).all(), f"step {t}: {name}"
+    p.close()
 
 
 @pytest.mark.parametrize("k,B,H,T,rb,policy", COPY_GATHER_CASES,
