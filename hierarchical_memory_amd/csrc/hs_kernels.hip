@@ -59,6 +59,7 @@ enum : int8_t { C_PAD = 0, C_BAD = 1, C_DUP = 2, C_RES = 3, C_CAND = 4 };
 constexpr int kStatusBadId = 1, kStatusDupId = 2, kStatusBadState = 4, kStatusStale = 8;
 constexpr int kUnroll = 4;  // 16-byte loads each thread keeps in flight in the gather loop
 constexpr int kCommitUnroll = 2;  // the same in the commit's row copy (measured: 2 beats 4 and 8)
+constexpr int kTailUnroll = 8;    // chunks each thread moves per pass when the tail window advances
 
 // misc words in LDS: one slot array of wave totals per block scan, per-wave flag words, then single words
 constexpr int kMiscScanSel = 0, kMiscScanRank = kWaves, kMiscScanTail = 2 * kWaves, kMiscWaveBad = 3 * kWaves,
@@ -1718,19 +1719,40 @@ __global__ __launch_bounds__(1024) void advance_tail_kernel(AdvanceTailArgs a) {
   int skipped = 0;
   // the ring row of token t0 + j is (t0 mod T) + j, wrapped once (j < n <= T)
   const int t0m = (int)((((int64_t)t0 % T) + T) % T);
-  for (int c = tid; c < n * row16; c += blockDim.x) {
-    const int j = c / row16, q = c - j * row16;
-    const int64_t x = (int64_t)t0 + j;
-    if (x < 0 || x >= a.H) {
-      skipped = 1;
-      continue;
+  // kTailUnroll chunks per thread per pass, every load (the ring row and the token's page entry) issued before
+  // any store (measured with 64 rows per request on 64 requests: 93.9 us one chunk at a time, 91.7 us with 8)
+  const int total = n * row16, nt = blockDim.x;
+  for (int c0 = tid; c0 < total; c0 += nt * kTailUnroll) {
+    v4u v[kTailUnroll];
+    int64_t xs[kTailUnroll];
+    int ss[kTailUnroll], qs[kTailUnroll];
+#pragma unroll
+    for (int u = 0; u < kTailUnroll; ++u) {
+      const int c = c0 + u * nt;
+      xs[u] = -1;
+      ss[u] = -1;
+      qs[u] = 0;
+      if (c < total) {
+        const int j = c / row16, q = c - j * row16;
+        const int64_t x = (int64_t)t0 + j;
+        if (x < 0 || x >= a.H) {
+          skipped = 1;
+          continue;
+        }
+        const uint32_t e = (uint32_t)t0m + (uint32_t)j;  // < 2T, exact in uint32
+        const uint32_t ring = e >= (uint32_t)T ? e - (uint32_t)T : e;
+        v[u] = tailr[(size_t)ring * row16 + q];
+        ss[u] = a.page[rH + x];
+        xs[u] = x;
+        qs[u] = q;
+      }
     }
-    const uint32_t e = (uint32_t)t0m + (uint32_t)j;  // < 2T, exact in uint32
-    const uint32_t ring = e >= (uint32_t)T ? e - (uint32_t)T : e;
-    const v4u v = tailr[(size_t)ring * row16 + q];
-    hostr[(size_t)x * row16 + q] = v;  // plain stores: non-temporal ones to host memory run ~10 % slower
-    const int s = a.page[rH + x];
-    if (s >= 0 && s < a.B) hotr[(size_t)s * row16 + q] = v;
+#pragma unroll
+    for (int u = 0; u < kTailUnroll; ++u) {
+      if (xs[u] < 0) continue;
+      hostr[(size_t)xs[u] * row16 + qs[u]] = v[u];  // plain stores: non-temporal ones to host memory run ~10 % slower
+      if (ss[u] >= 0 && ss[u] < a.B) hotr[(size_t)ss[u] * row16 + qs[u]] = v[u];
+    }
   }
   skipped = __syncthreads_or(skipped);
   if (tid == 0) {
